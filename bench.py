@@ -1,0 +1,222 @@
+"""Benchmark of the FGP step on one MI355X.
+
+Prints one JSON line.  A "step" is one FGP step over the whole volume (one
+launch of the fused kernel); the default workload is the 512^3 ellipsoid
+phantom, 20 outer x 10 inner steps, lambda = 0.002.  The timed region runs
+exactly --steps steps (in outer iterations of 10, momentum restarted at each)
+on one stream, bracketed by device synchronisation; inputs are resident in
+HBM before it starts.
+
+Besides the headline ms/step it reports:
+  roofline      algorithmic bytes per launch (52 B per voxel: read b, r (3),
+                p (3); write p (3), r (3)) over the average launch duration,
+                timed with events around every launch on the launch stream,
+                against MI355X's 8 TB/s HBM peak; `traffic` is the HBM bytes
+                per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+                committed under profiles/ (null when the kernel sources have
+                changed since those counters were taken)
+  copy          bandwidth of a plain device copy of 2 x 1 GiB on the same box
+  cpu_baseline  the CPU oracle (fp32, OpenMP) timed on the host cores on a
+                bounded sample: the first outer iteration (10 steps) of the
+                same workload at full size
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+HBM_PEAK_GBS = 8000.0
+BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "two_kernel": 72}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_512.json")
+METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
+
+
+def kernel_source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "stencil_dual_update_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(variant, workload):
+    """HBM bytes per launch from the committed counter summary, if current."""
+    if variant != "fused" or workload != 3 or not os.path.exists(TRAFFIC_FILE):
+        return None
+    with open(TRAFFIC_FILE) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256") != kernel_source_digest():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--variant", default="fused",
+                    choices=["fused", "lds_march", "two_kernel", "point"])
+    ap.add_argument("--no-cpu-baseline", action="store_true",
+                    help="skip the CPU oracle leg")
+    ap.add_argument("--no-copy", action="store_true", help="skip the copy probe")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(the step would shard by z-slabs with a one-plane halo; not built). "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+    import numpy as np
+    import torch
+
+    import phantoms
+    import stencil_dual_update_amd as tvf
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    w = phantoms.workload(args.workload)
+    nx, ny, nz = w["dims"]
+    lam = w["lam"]
+    n_inner = w["n_inner"]
+    variant = tvf.VARIANTS[args.variant]
+    nvox = nx * ny * nz
+
+    t0 = time.time()
+    b_host, p0_host, _ = phantoms.make_inputs(args.workload)
+    gen_s = time.time() - t0
+    b = torch.from_numpy(b_host).to(dev)
+    p = torch.from_numpy(p0_host).to(dev)
+    ra = p.clone()
+    rb = torch.empty_like(ra)
+    ws = torch.empty_like(b) if variant == tvf.TWO_KERNEL else None
+    stream = torch.cuda.Stream(device=dev)
+    torch.cuda.synchronize()
+
+    def run_steps(k, r_cur, r_nxt):
+        """k steps in outer iterations of n_inner; returns (r_cur, r_nxt) after."""
+        full, rest = divmod(k, n_inner)
+        for n_outer, ni in ((full, n_inner), (1 if rest else 0, rest)):
+            if n_outer * ni == 0:
+                continue
+            where = tvf.tv_fgp_run(b, p, r_cur, r_nxt, lam, n_outer, ni,
+                                   variant=variant, z_ws=ws, stream=stream)
+            if where:
+                r_cur, r_nxt = r_nxt, r_cur
+        return r_cur, r_nxt
+
+    with torch.cuda.stream(stream):
+        r_cur, r_nxt = run_steps(args.warmup, ra, rb)
+        torch.cuda.synchronize()
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        t_wall = time.perf_counter()
+        start.record(stream)
+        r_cur, r_nxt = run_steps(args.steps, r_cur, r_nxt)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t_wall) * 1e3
+        region_ms = start.elapsed_time(stop)
+
+        # per-launch durations: an event pair around every launch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for k in range(args.steps):
+            m = tvf.momentum(k % n_inner + 1)
+            evs[k][0].record(stream)
+            tvf.tv_fgp_step(b, p, r_cur, r_nxt, lam, m, variant=variant, z_ws=ws,
+                            stream=stream)
+            evs[k][1].record(stream)
+            r_cur, r_nxt = r_nxt, r_cur
+        torch.cuda.synchronize()
+        launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
+
+    ms_per_step = region_ms / args.steps
+    step_bytes = BYTES_PER_VOXEL[args.variant] * nvox
+    launch_avg_ms = float(np.mean(launch_ms))
+    achieved = step_bytes / (launch_avg_ms * 1e-3) / 1e9
+    region_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+
+    copy = None
+    if not args.no_copy:
+        src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            reps = 20
+            for _ in range(reps):
+                dst.copy_(src)
+            c1.record(stream)
+            torch.cuda.synchronize()
+        copy_ms = c0.elapsed_time(c1) / reps
+        copy = {"bytes": 2 * src.numel() * 4, "ms": round(copy_ms, 4),
+                "gbps": round(2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1)}
+        del src, dst
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+        threads = min(16, os.cpu_count() or 1)
+        oracle.set_threads(threads)
+        p0 = p0_host
+        t1 = time.perf_counter()
+        oracle.run(b_host, p0, p0, lam, 1, n_inner)
+        cpu_s = time.perf_counter() - t1
+        cpu = {"value": round(cpu_s * 1e3 / n_inner, 3), "unit": "ms/step",
+               "cores": oracle.get_threads(), "kind": "oracle",
+               "sample": "first outer iteration (%d steps) of the same workload at "
+                         "full size, fp32 exact-order oracle, %.1f s" % (n_inner, cpu_s)}
+
+    traffic = measured_traffic(args.variant, args.workload)
+    out = {
+        "metric": METRIC,
+        "value": round(ms_per_step, 5),
+        "unit": "ms/step",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": phantoms.NAMES[args.workload],
+                   "dims": [nx, ny, nz], "lambda": lam, "steps_per_outer": n_inner,
+                   "variant": args.variant, "parallelism": "single GPU"},
+        "gbps": round(region_gbs, 1),
+        "pct_hbm_peak": round(100.0 * region_gbs / HBM_PEAK_GBS, 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "algorithmic_bytes_per_launch": step_bytes,
+                     "launch_ms_avg": round(launch_avg_ms, 5),
+                     "launch_ms_min": round(float(np.min(launch_ms)), 5),
+                     "launch_ms_max": round(float(np.max(launch_ms)), 5)},
+        "copy": copy,
+        "pct_of_copy": (round(100.0 * region_gbs / copy["gbps"], 1) if copy else None),
+        "cpu_baseline": cpu,
+        "wall_ms_timed_region": round(wall_ms, 2),
+        "input_gen_s": round(gen_s, 2),
+        "device": torch.cuda.get_device_name(dev),
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

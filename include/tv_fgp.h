@@ -1,0 +1,154 @@
+/*
+ * tv_fgp.h — C ABI of the MI355X (gfx950) FGP step on the 3D total-variation
+ * dual.
+ *
+ * The operation is the one described on the page "TV solver: the FGP step on
+ * the GPU", section "What one step does".  For every voxel i, with b the input
+ * volume, r the momentum copy of the dual and p the dual (three components
+ * each):
+ *     z(j)  = max(b(j) - lambda * L(r)(j), 0),
+ *             L(r)(j) = sum over axes a of r_a(j) - r_a(j - e_a)
+ *     g_a   = z(i) - z(i + e_a)
+ *     q     = r(i) + g / (12 lambda)
+ *     p'    = q / max(1, |q|)        (|q|: Euclidean norm of the 3-vector)
+ *     r(i)  = p' + m (p' - p(i)),  p(i) = p'
+ * Boundary rule (the page does not state one): r_a(j - e_a) is 0 below the
+ * lower a-face, and g_a is 0 at the upper a-face.
+ *
+ * Conventions shared by every entry point:
+ *   - All data pointers are DEVICE pointers (memory on the current HIP
+ *     device), owned by the caller.  The library never allocates or frees.
+ *   - A volume is nx*ny*nz contiguous floats, x fastest: voxel (x, y, z) is at
+ *     index x + nx*(y + ny*z).  A vector field is three such volumes passed as
+ *     an array of three pointers, component 0 along x, 1 along y, 2 along z.
+ *   - Arithmetic is IEEE fp32 with round-to-nearest, no fused multiply-add,
+ *     correctly rounded square root and division; every variant evaluates the
+ *     same expressions in the same order, so all variants give the same bits.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
+ *     Calls return as soon as the work is enqueued; they never synchronise
+ *     the host.  Results are valid once the stream has completed.
+ *   - Errors are negative status codes (below); nothing is enqueued when a
+ *     call fails validation.  No call aborts, throws or prints.  NaN or Inf
+ *     in the data is not checked; it propagates.
+ *   - Concurrent calls that write the same buffers race; the caller orders
+ *     them (same stream, or events).
+ */
+#ifndef TV_FGP_H
+#define TV_FGP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define TV_OK             0
+#define TV_ERR_NULL      -1  /* a required pointer is NULL                           */
+#define TV_ERR_DIMS      -2  /* a dimension < 1, or nx*ny*nz*4 bytes overflows        */
+#define TV_ERR_ALIAS     -3  /* a written buffer overlaps another buffer of the call  */
+#define TV_ERR_PARAM     -4  /* lambda <= 0 or not finite, 1/(12 lambda) not finite,
+                                m not finite, negative step counts                   */
+#define TV_ERR_WORKSPACE -5  /* the two-kernel variant was given no z workspace       */
+#define TV_ERR_VARIANT   -6  /* unknown variant                                      */
+#define TV_ERR_LAUNCH    -7  /* the HIP runtime reported an error at a launch         */
+#define TV_ERR_ALIGN     -8  /* a pointer is not 4-byte aligned                       */
+
+/* Kernel variants.  All give bit-identical results. */
+#define TV_FGP_FUSED      0  /* default: one fused pass; each thread walks a column
+                                along z and carries z and r between planes           */
+#define TV_FGP_LDS_MARCH  1  /* ablation: an x-y tile marches along z with the
+                                planes of r and z staged in LDS                      */
+#define TV_FGP_TWO_KERNEL 2  /* ablation: a primal kernel writes z to the workspace,
+                                a dual kernel reads it (18 volumes per step)         */
+#define TV_FGP_POINT      3  /* ablation: one voxel per thread, z recomputed at the
+                                voxel and its three upper neighbours                 */
+
+/*
+ * One FGP step ("TV solver: the FGP step on the GPU", section "What one step
+ * does") with the default fused variant.
+ *   b       [in]      volume b (nx*ny*nz floats).
+ *   p       [in/out]  the dual, three volumes; overwritten with p'.
+ *   r_in    [in]      momentum copy read by the step, three volumes.
+ *   r_out   [out]     new momentum copy p' + m (p' - p), three volumes.
+ *   lambda  [in]      regularisation weight, finite and > 0; the dual step
+ *                     size is c = 1/(12 lambda), rounded in fp32 as
+ *                     1.0f / (12.0f * lambda).
+ *   m       [in]      momentum coefficient of this step, finite.
+ *   nx, ny, nz        dimensions, each >= 1.
+ *   stream            hipStream_t to enqueue on.
+ * p, r_out must not overlap each other or b, r_in (r_in is still read by
+ * neighbouring voxels while r_out is written, hence the two buffers).
+ * Returns TV_OK or a negative status.
+ */
+int tv_fgp_step(const float *b, float *const p[3], const float *const r_in[3],
+                float *const r_out[3], float lambda, float m,
+                int64_t nx, int64_t ny, int64_t nz, void *stream);
+
+/*
+ * tv_fgp_step with an explicit variant (TV_FGP_*).  z_ws is a device buffer
+ * of at least tv_fgp_workspace_bytes(variant, ...) bytes; it is required by
+ * TV_FGP_TWO_KERNEL (which leaves the primal z of r in it) and ignored
+ * (may be NULL) otherwise.  Same page and section as tv_fgp_step.
+ */
+int tv_fgp_step_ex(const float *b, float *const p[3],
+                   const float *const r_in[3], float *const r_out[3],
+                   float lambda, float m, int64_t nx, int64_t ny, int64_t nz,
+                   int variant, float *z_ws, void *stream);
+
+/*
+ * The inner loop of the solver: n_outer outer iterations of n_inner FGP
+ * steps ("TV solver: the FGP step on the GPU", opening paragraph: an outer
+ * iteration runs tv_inner FGP steps).  The momentum sequence is the FISTA
+ * one, restarted at every outer iteration:
+ *     t_1 = 1,  t_{k+1} = (1 + sqrt(1 + 4 t_k^2)) / 2,
+ *     m_k = (t_k - 1) / t_{k+1}   (computed in double, rounded once to fp32)
+ * for the k-th step of each outer iteration (m_1 = 0).  p and r carry over
+ * between outer iterations.
+ *   r_a, r_b  [in/out]  the two momentum buffers; the first step reads r_a.
+ *                       After every step the roles swap.
+ *   r_final   [out]     host pointer, may be NULL; receives 0 if the last
+ *                       momentum copy is in r_a, 1 if in r_b.
+ * With n_outer * n_inner == 0 nothing is enqueued and *r_final = 0.
+ * Other arguments as tv_fgp_step_ex.  p, r_a, r_b and z_ws must not overlap
+ * each other or b.
+ */
+int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
+               float *const r_b[3], float lambda, int n_outer, int n_inner,
+               int64_t nx, int64_t ny, int64_t nz, int variant, float *z_ws,
+               void *stream, int *r_final);
+
+/*
+ * Primal read-out z = max(b - lambda * L(p), 0) from a dual field p, with the
+ * same expression and boundary rule as the step ("TV solver: the FGP step on
+ * the GPU", section "What one step does", first formula).
+ *   z [out] nx*ny*nz floats; must not overlap b or p.
+ */
+int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
+              int64_t nx, int64_t ny, int64_t nz, void *stream);
+
+/*
+ * Bytes of z workspace `variant` needs at these dimensions: nx*ny*nz*4 for
+ * TV_FGP_TWO_KERNEL, 0 for the others.  Returns 0 for invalid dimensions or
+ * an unknown variant.
+ */
+size_t tv_fgp_workspace_bytes(int variant, int64_t nx, int64_t ny, int64_t nz);
+
+/*
+ * m_k used by tv_fgp_run for the k-th step of an outer iteration (k >= 1),
+ * as the fp32 value passed to the kernels; 0 for k < 1.  Host-only.
+ */
+float tv_fgp_momentum(int k);
+
+/* Static, NUL-terminated description of a status code. */
+const char *tv_fgp_status_string(int status);
+
+/* Name of a variant ("fused", "lds_march", "two_kernel", "point"), or NULL. */
+const char *tv_fgp_variant_name(int variant);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TV_FGP_H */

@@ -1,0 +1,202 @@
+"""ctypes binding of libtvfgp.so (the C ABI declared in include/tv_fgp.h).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI.  torch tensors supply device memory and the
+stream; their data pointers are passed through unchanged.  There is no CPU
+fallback: importing this module fails if the library has not been built.
+"""
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libtvfgp.so")
+
+TV_OK = 0
+TV_ERR_NULL = -1
+TV_ERR_DIMS = -2
+TV_ERR_ALIAS = -3
+TV_ERR_PARAM = -4
+TV_ERR_WORKSPACE = -5
+TV_ERR_VARIANT = -6
+TV_ERR_LAUNCH = -7
+TV_ERR_ALIGN = -8
+
+FUSED = 0
+LDS_MARCH = 1
+TWO_KERNEL = 2
+POINT = 3
+VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
+            "point": POINT}
+
+# Names declared in include/tv_fgp.h, in declaration order.
+EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_primal",
+           "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_status_string",
+           "tv_fgp_variant_name")
+
+
+class TvFgpError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s failed: %s (%d)" % (where, status_string(status), status))
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            "libtvfgp.so is not built (expected at %s); run "
+            "`python -c 'import __graft_entry__ as g; g.build()'` or "
+            "`python stencil_dual_update_amd/build_lib.py`" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.c_void_p
+    P3 = ctypes.POINTER(ctypes.c_void_p)  # float *const x[3]; NULL allowed
+    I64 = ctypes.c_int64
+    F = ctypes.c_float
+    lib.tv_fgp_step.restype = ctypes.c_int
+    lib.tv_fgp_step.argtypes = [P, P3, P3, P3, F, F, I64, I64, I64, P]
+    lib.tv_fgp_step_ex.restype = ctypes.c_int
+    lib.tv_fgp_step_ex.argtypes = [P, P3, P3, P3, F, F, I64, I64, I64,
+                                   ctypes.c_int, P, P]
+    lib.tv_fgp_run.restype = ctypes.c_int
+    lib.tv_fgp_run.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int,
+                               I64, I64, I64, ctypes.c_int, P, P,
+                               ctypes.POINTER(ctypes.c_int)]
+    lib.tv_primal.restype = ctypes.c_int
+    lib.tv_primal.argtypes = [P, P3, P, F, I64, I64, I64, P]
+    lib.tv_fgp_workspace_bytes.restype = ctypes.c_size_t
+    lib.tv_fgp_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
+    lib.tv_fgp_momentum.restype = ctypes.c_float
+    lib.tv_fgp_momentum.argtypes = [ctypes.c_int]
+    lib.tv_fgp_status_string.restype = ctypes.c_char_p
+    lib.tv_fgp_status_string.argtypes = [ctypes.c_int]
+    lib.tv_fgp_variant_name.restype = ctypes.c_char_p
+    lib.tv_fgp_variant_name.argtypes = [ctypes.c_int]
+    return lib
+
+
+lib = _load()
+
+
+def status_string(status):
+    return lib.tv_fgp_status_string(int(status)).decode()
+
+
+def variant_name(variant):
+    s = lib.tv_fgp_variant_name(int(variant))
+    return None if s is None else s.decode()
+
+
+def momentum(k):
+    """m_k as the fp32 value the library passes to its kernels."""
+    return float(lib.tv_fgp_momentum(int(k)))
+
+
+def workspace_bytes(variant, nx, ny, nz):
+    return int(lib.tv_fgp_workspace_bytes(int(variant), nx, ny, nz))
+
+
+# --------------------------------------------------------------------------
+# marshalling helpers
+
+def _addr(t):
+    """Device address of a tensor (or a raw integer address, or None)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _check_volume(t, shape, what):
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % what)
+    if t.dtype != torch.float32:
+        raise ValueError("%s must be float32" % what)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    if tuple(t.shape) != shape:
+        raise ValueError("%s has shape %s, expected %s" % (what, tuple(t.shape), shape))
+
+
+def _field(f, shape, what):
+    """Three component addresses of a vector field.
+
+    ``f`` is a (3, nz, ny, nx) tensor, a sequence of three (nz, ny, nx)
+    tensors, or a sequence of three raw addresses.
+    """
+    if f is None:
+        return (ctypes.c_void_p * 3)(None, None, None)
+    comps = [f[0], f[1], f[2]] if not isinstance(f, (list, tuple)) else list(f)
+    if len(comps) != 3:
+        raise ValueError("%s needs three components" % what)
+    for a, c in enumerate(comps):
+        _check_volume(c, shape, "%s[%d]" % (what, a))
+    return (ctypes.c_void_p * 3)(*[_addr(c) for c in comps])
+
+
+def _dims_of(b, dims):
+    if dims is not None:
+        nx, ny, nz = dims
+        return int(nx), int(ny), int(nz)
+    nz, ny, nx = b.shape
+    return int(nx), int(ny), int(nz)
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _raise(status, where):
+    if status != TV_OK:
+        raise TvFgpError(status, where)
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+
+def tv_fgp_step(b, p, r_in, r_out, lam, m, variant=FUSED, z_ws=None,
+                stream=None, dims=None):
+    """One FGP step; p is updated in place, the new momentum copy goes to r_out."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_volume(z_ws, shape, "z_ws")
+    st = lib.tv_fgp_step_ex(_addr(b), _field(p, shape, "p"),
+                            _field(r_in, shape, "r_in"),
+                            _field(r_out, shape, "r_out"), float(lam), float(m),
+                            nx, ny, nz, int(variant), _addr(z_ws), _stream(stream))
+    _raise(st, "tv_fgp_step")
+
+
+def tv_fgp_run(b, p, r_a, r_b, lam, n_outer, n_inner, variant=FUSED, z_ws=None,
+               stream=None, dims=None):
+    """n_outer x n_inner FGP steps; returns 0 if the last r is in r_a, 1 if in r_b."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_volume(z_ws, shape, "z_ws")
+    where = ctypes.c_int(-1)
+    st = lib.tv_fgp_run(_addr(b), _field(p, shape, "p"), _field(r_a, shape, "r_a"),
+                        _field(r_b, shape, "r_b"), float(lam), int(n_outer),
+                        int(n_inner), nx, ny, nz, int(variant), _addr(z_ws),
+                        _stream(stream), ctypes.byref(where))
+    _raise(st, "tv_fgp_run")
+    return where.value
+
+
+def tv_primal(b, p, z, lam, stream=None, dims=None):
+    """z = max(b - lam*L(p), 0) into the caller's buffer z."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_volume(z, shape, "z")
+    st = lib.tv_primal(_addr(b), _field(p, shape, "p"), _addr(z), float(lam),
+                       nx, ny, nz, _stream(stream))
+    _raise(st, "tv_primal")

@@ -1,0 +1,56 @@
+// Internal interface between the C-ABI layer (argument checks, momentum
+// schedule, buffer ping-pong) and the kernel launchers.  Arguments reaching
+// a launcher have been validated: pointers non-null, aligned and disjoint,
+// dimensions >= 1, parameters finite.
+#pragma once
+
+#include <stdint.h>
+
+namespace tvfgp {
+
+constexpr int kVariantFused = 0;
+constexpr int kVariantLdsMarch = 1;
+constexpr int kVariantTwoKernel = 2;
+constexpr int kVariantPoint = 3;
+constexpr int kNumVariants = 4;
+
+constexpr int kLaunchFailed = -1;
+
+// Planes along z that one thread (or one tile) walks in the marching kernels.
+constexpr int64_t kDefaultPlanes = 16;
+
+struct StepArgs {
+  const float *b;
+  float *p[3];
+  const float *r_in[3];
+  float *r_out[3];
+  float *z_ws;       // two-kernel variant only
+  float lam;         // lambda
+  float c;           // 1 / (12 lambda), rounded in fp32
+  float m;           // momentum coefficient
+  int64_t nx, ny, nz;
+  int64_t planes;    // planes per tile along z
+  int variant;
+  void *stream;      // hipStream_t
+};
+
+struct PrimalArgs {
+  const float *b;
+  const float *p[3];
+  float *z;
+  float lam;
+  int64_t nx, ny, nz;
+  int64_t planes;
+  void *stream;
+};
+
+// Enqueue one step / one read-out.  Return 0, or kLaunchFailed when the HIP
+// runtime reports an error after a launch.
+int launch_step(const StepArgs &a);
+int launch_primal(const PrimalArgs &a);
+int launch_lds_march(const StepArgs &a);
+
+// True when every index the kernels form at these dimensions fits in int32.
+bool fits_int32(int64_t nx, int64_t ny, int64_t nz);
+
+}  // namespace tvfgp

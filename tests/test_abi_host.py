@@ -1,0 +1,205 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+The library must load, export every function include/tv_fgp.h declares, and
+reject every invalid call with its documented status before touching the HIP
+runtime.  The momentum schedule is host logic and is compared with the
+oracle's independent implementation.  Fake device addresses are used only on
+paths that fail validation (or enqueue nothing), so no memory is accessed.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+tvf = pytest.importorskip("stencil_dual_update_amd", reason="libtvfgp.so not built")
+L = tvf.lib
+
+NX, NY, NZ = 8, 6, 5
+VOL = NX * NY * NZ * 4
+BASE = 1 << 40  # fake, never dereferenced
+
+
+def addr(k):
+    """Address of the k-th fake volume (disjoint, 256-byte aligned)."""
+    return BASE + k * ((VOL + 255) // 256 * 256 + 4096)
+
+
+P3 = ctypes.c_void_p * 3
+
+
+def field(*ks):
+    return P3(*[None if k is None else addr(k) if isinstance(k, int) and k < 1000 else k
+                for k in ks])
+
+
+def step(b=0, p=(1, 2, 3), ri=(4, 5, 6), ro=(7, 8, 9), lam=0.01, m=0.0,
+         dims=(NX, NY, NZ), variant=0, ws=None):
+    bb = None if b is None else addr(b)
+    pp = None if p is None else field(*p)
+    rin = None if ri is None else field(*ri)
+    rout = None if ro is None else field(*ro)
+    return L.tv_fgp_step_ex(bb, pp, rin, rout, lam, m, *dims, variant,
+                            None if ws is None else addr(ws), None)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "tv_fgp.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"\b(tv_\w+)\s*\(", text)
+
+
+def test_exports_match_header():
+    names = header_functions()
+    assert names, "no declarations parsed"
+    assert tuple(names) == tvf.EXPORTS
+    for n in names:
+        assert hasattr(L, n), n
+        assert ctypes.cast(getattr(L, n), ctypes.c_void_p).value
+
+
+def test_library_path_is_in_tree():
+    assert os.path.dirname(tvf.LIB_PATH) == os.path.join(ROOT, "stencil_dual_update_amd")
+
+
+def test_momentum_matches_oracle(oracle_mod):
+    for k in range(1, 60):
+        assert np.float32(tvf.momentum(k)) == oracle_mod.momentum_f32(k), k
+    assert tvf.momentum(0) == 0.0 and tvf.momentum(-3) == 0.0
+
+
+def test_status_strings_distinct():
+    codes = [0, -1, -2, -3, -4, -5, -6, -7, -8]
+    strs = [tvf.status_string(c) for c in codes]
+    assert len(set(strs)) == len(strs)
+    assert tvf.status_string(-99) == "unknown status"
+
+
+def test_variant_names():
+    for name, v in tvf.VARIANTS.items():
+        assert tvf.variant_name(v) == name
+    assert tvf.variant_name(9) is None
+
+
+def test_workspace_bytes():
+    assert tvf.workspace_bytes(tvf.TWO_KERNEL, 10, 20, 30) == 10 * 20 * 30 * 4
+    for v in (tvf.FUSED, tvf.LDS_MARCH, tvf.POINT):
+        assert tvf.workspace_bytes(v, 10, 20, 30) == 0
+    assert tvf.workspace_bytes(tvf.TWO_KERNEL, 0, 20, 30) == 0
+    assert tvf.workspace_bytes(7, 10, 20, 30) == 0
+    assert tvf.workspace_bytes(tvf.TWO_KERNEL, 1 << 31, 1 << 31, 1 << 31) == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=None), tvf.TV_ERR_NULL),
+    (dict(p=None), tvf.TV_ERR_NULL),
+    (dict(ri=None), tvf.TV_ERR_NULL),
+    (dict(ro=None), tvf.TV_ERR_NULL),
+    (dict(p=(1, None, 3)), tvf.TV_ERR_NULL),
+    (dict(ro=(7, 8, None)), tvf.TV_ERR_NULL),
+    (dict(dims=(0, NY, NZ)), tvf.TV_ERR_DIMS),
+    (dict(dims=(NX, -1, NZ)), tvf.TV_ERR_DIMS),
+    (dict(dims=(NX, NY, 0)), tvf.TV_ERR_DIMS),
+    (dict(dims=(1 << 31, 1 << 31, 1 << 31)), tvf.TV_ERR_DIMS),
+    (dict(dims=(1 << 62, 2, 1)), tvf.TV_ERR_DIMS),
+    (dict(ro=(7, 8, 5)), tvf.TV_ERR_ALIAS),        # r_out aliases r_in
+    (dict(ro=(7, 7, 9)), tvf.TV_ERR_ALIAS),        # two outputs alias
+    (dict(p=(1, 2, 0)), tvf.TV_ERR_ALIAS),         # p aliases b
+    (dict(p=(4, 2, 3)), tvf.TV_ERR_ALIAS),         # p aliases r_in
+    (dict(ro=(7, 8, 1)), tvf.TV_ERR_ALIAS),        # r_out aliases p
+    (dict(lam=0.0), tvf.TV_ERR_PARAM),
+    (dict(lam=-0.01), tvf.TV_ERR_PARAM),
+    (dict(lam=float("nan")), tvf.TV_ERR_PARAM),
+    (dict(lam=float("inf")), tvf.TV_ERR_PARAM),
+    (dict(lam=1e-45), tvf.TV_ERR_PARAM),           # 1/(12 lambda) overflows
+    (dict(m=float("nan")), tvf.TV_ERR_PARAM),
+    (dict(m=float("inf")), tvf.TV_ERR_PARAM),
+    (dict(variant=4), tvf.TV_ERR_VARIANT),
+    (dict(variant=-1), tvf.TV_ERR_VARIANT),
+    (dict(variant=2), tvf.TV_ERR_WORKSPACE),       # two-kernel without z
+    (dict(variant=2, ws=0), tvf.TV_ERR_ALIAS),     # workspace aliases b
+])
+def test_step_rejects(kw, code):
+    assert step(**kw) == code
+
+
+def test_partial_overlap_is_alias():
+    pp = field(1, 2, 3)
+    ri = field(4, 5, 6)
+    ro = P3(addr(7), addr(8), addr(5) + 8)  # overlaps r_in[1] by all but 8 bytes
+    assert L.tv_fgp_step_ex(addr(0), pp, ri, ro, 0.01, 0.0, NX, NY, NZ, 0, None, None) \
+        == tvf.TV_ERR_ALIAS
+    ro = P3(addr(7), addr(8), addr(5) + VOL - 4)  # last float of r_in[1]
+    assert L.tv_fgp_step_ex(addr(0), pp, ri, ro, 0.01, 0.0, NX, NY, NZ, 0, None, None) \
+        == tvf.TV_ERR_ALIAS
+
+
+def test_misaligned_pointer():
+    pp = P3(addr(1) + 2, addr(2), addr(3))
+    assert L.tv_fgp_step_ex(addr(0), pp, field(4, 5, 6), field(7, 8, 9), 0.01, 0.0,
+                            NX, NY, NZ, 0, None, None) == tvf.TV_ERR_ALIGN
+
+
+def test_default_entry_point_validates():
+    assert L.tv_fgp_step(None, field(1, 2, 3), field(4, 5, 6), field(7, 8, 9),
+                         0.01, 0.0, NX, NY, NZ, None) == tvf.TV_ERR_NULL
+    assert L.tv_fgp_step(addr(0), field(1, 2, 3), field(4, 5, 6), field(7, 8, 9),
+                         0.01, 0.0, NX, NY, 0, None) == tvf.TV_ERR_DIMS
+
+
+def run(b=0, p=(1, 2, 3), ra=(4, 5, 6), rb=(7, 8, 9), lam=0.01, n_outer=2, n_inner=3,
+        dims=(NX, NY, NZ), variant=0, ws=None):
+    where = ctypes.c_int(-7)
+    st = L.tv_fgp_run(None if b is None else addr(b), field(*p), field(*ra), field(*rb),
+                      lam, n_outer, n_inner, *dims, variant,
+                      None if ws is None else addr(ws), None, ctypes.byref(where))
+    return st, where.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=None), tvf.TV_ERR_NULL),
+    (dict(n_outer=-1), tvf.TV_ERR_PARAM),
+    (dict(n_inner=-2), tvf.TV_ERR_PARAM),
+    (dict(lam=0.0), tvf.TV_ERR_PARAM),
+    (dict(rb=(7, 8, 4)), tvf.TV_ERR_ALIAS),        # r_b aliases r_a
+    (dict(ra=(4, 5, 1)), tvf.TV_ERR_ALIAS),        # r_a aliases p
+    (dict(dims=(NX, NY, -4)), tvf.TV_ERR_DIMS),
+    (dict(variant=5), tvf.TV_ERR_VARIANT),
+    (dict(variant=2), tvf.TV_ERR_WORKSPACE),
+])
+def test_run_rejects(kw, code):
+    st, where = run(**kw)
+    assert st == code
+    assert where == 0
+
+
+@pytest.mark.parametrize("n_outer,n_inner", [(0, 10), (20, 0), (0, 0)])
+def test_run_with_no_steps_enqueues_nothing(n_outer, n_inner):
+    # valid arguments, zero steps: returns at once with r_final = 0 and never
+    # reaches the HIP runtime (there is no GPU here)
+    st, where = run(n_outer=n_outer, n_inner=n_inner)
+    assert st == tvf.TV_OK and where == 0
+
+
+def test_primal_rejects():
+    pp = field(1, 2, 3)
+    assert L.tv_primal(None, pp, addr(4), 0.01, NX, NY, NZ, None) == tvf.TV_ERR_NULL
+    assert L.tv_primal(addr(0), pp, None, 0.01, NX, NY, NZ, None) == tvf.TV_ERR_NULL
+    assert L.tv_primal(addr(0), None, addr(4), 0.01, NX, NY, NZ, None) == tvf.TV_ERR_NULL
+    assert L.tv_primal(addr(0), pp, addr(2), 0.01, NX, NY, NZ, None) == tvf.TV_ERR_ALIAS
+    assert L.tv_primal(addr(0), pp, addr(0), 0.01, NX, NY, NZ, None) == tvf.TV_ERR_ALIAS
+    assert L.tv_primal(addr(0), pp, addr(4), -1.0, NX, NY, NZ, None) == tvf.TV_ERR_PARAM
+    assert L.tv_primal(addr(0), pp, addr(4), 0.01, NX, 0, NZ, None) == tvf.TV_ERR_DIMS
+
+
+def test_python_binding_raises():
+    with pytest.raises(tvf.TvFgpError) as e:
+        tvf.tv_fgp_step(addr(0), [addr(1), addr(2), addr(3)], [addr(4), addr(5), addr(6)],
+                        [addr(7), addr(8), addr(5)], 0.01, 0.0, stream=0, dims=(NX, NY, NZ))
+    assert e.value.status == tvf.TV_ERR_ALIAS
+    assert tvf.tv_fgp_run(addr(0), [addr(1), addr(2), addr(3)], [addr(4), addr(5), addr(6)],
+                          [addr(7), addr(8), addr(9)], 0.01, 0, 10, stream=0,
+                          dims=(NX, NY, NZ)) == 0

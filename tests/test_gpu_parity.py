@@ -1,0 +1,320 @@
+"""GPU parity: the HIP kernels against the fp32 CPU oracle, element by element.
+
+Gate (all variants): max |GPU - oracle| <= 1e-5 on p, r and z after the
+full iteration count.  The kernels and the oracle evaluate the same fp32
+operations in the same order without contraction, so the expected result is
+bit-for-bit equality; the bitwise checks are separate tests so a one-ulp
+difference is reported as such rather than hidden behind the tolerance.
+Every call goes through the C ABI (libtvfgp.so via the ctypes binding).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import phantoms
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+VARIANTS = ["fused", "lds_march", "two_kernel", "point"]
+
+
+@pytest.fixture(scope="module")
+def tvf():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import stencil_dual_update_amd as m
+    oracle.set_threads(16)
+    return m
+
+
+def gpu_solve(tvf, b, p0, r0, lam, n_outer, n_inner, variant="fused", stream=None):
+    v = tvf.VARIANTS[variant]
+    dev = torch.device("cuda")
+    bt = torch.from_numpy(np.ascontiguousarray(b)).to(dev)
+    p = torch.from_numpy(np.ascontiguousarray(p0)).to(dev)
+    ra = torch.from_numpy(np.ascontiguousarray(r0)).to(dev)
+    rb = torch.full_like(ra, float("nan"))
+    ws = torch.empty_like(bt) if v == tvf.TWO_KERNEL else None
+    where = tvf.tv_fgp_run(bt, p, ra, rb, lam, n_outer, n_inner, variant=v, z_ws=ws,
+                           stream=stream)
+    r = rb if where else ra
+    z = torch.empty_like(bt)
+    tvf.tv_primal(bt, p, z, lam, stream=stream)
+    torch.cuda.synchronize()
+    out = p.cpu().numpy(), r.cpu().numpy(), z.cpu().numpy()
+    del bt, p, ra, rb, ws, z
+    return out
+
+
+def oracle_solve(b, p0, r0, lam, n_outer, n_inner):
+    p, r = oracle.run(b, p0, r0, lam, n_outer, n_inner)
+    return p, r, oracle.primal(b, p, lam)
+
+
+def max_abs(a, e):
+    return float(np.max(np.abs(a.astype(np.float64) - e.astype(np.float64)))) if a.size else 0.0
+
+
+def assert_close(got, exp, label):
+    for name, g, e in zip("prz", got, exp):
+        assert g.shape == e.shape
+        assert np.isfinite(g).all(), "%s %s: non-finite values" % (label, name)
+        d = max_abs(g, e)
+        assert d <= TOL, "%s %s: max abs %.3g > %g" % (label, name, d, TOL)
+
+
+def assert_bitwise(got, exp, label):
+    for name, g, e in zip("prz", got, exp):
+        neq = int(np.count_nonzero(g.view(np.uint32) != e.view(np.uint32)))
+        assert neq == 0, "%s %s: %d of %d elements differ in bits (max abs %.3g)" % (
+            label, name, neq, g.size, max_abs(g, e))
+
+
+_cache = {}
+
+
+def reference(idx, dims=None, n_outer=None, n_inner=None):
+    w = phantoms.workload(idx)
+    n_outer = w["n_outer"] if n_outer is None else n_outer
+    n_inner = w["n_inner"] if n_inner is None else n_inner
+    key = (idx, dims, n_outer, n_inner)
+    if key not in _cache:
+        b, p0, r0 = phantoms.make_inputs(idx, dims)
+        _cache.clear()
+        _cache[key] = (b, p0, r0, w["lam"], n_outer, n_inner,
+                       oracle_solve(b, p0, r0, w["lam"], n_outer, n_inner))
+    return _cache[key]
+
+
+# --------------------------------------------------------------------------
+# small workloads, every variant
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_workload0_blobs_32(tvf, variant):
+    b, p0, r0, lam, no, ni, exp = reference(0)
+    got = gpu_solve(tvf, b, p0, r0, lam, no, ni, variant)
+    assert_close(got, exp, "blobs 32^3 " + variant)
+    assert_bitwise(got, exp, "blobs 32^3 " + variant)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_workload1_blobs_128_full_200_steps(tvf, variant):
+    b, p0, r0, lam, no, ni, exp = reference(1)
+    got = gpu_solve(tvf, b, p0, r0, lam, no, ni, variant)
+    assert_close(got, exp, "blobs 128^3 " + variant)
+    assert_bitwise(got, exp, "blobs 128^3 " + variant)
+
+
+RAGGED = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70),
+          (65, 5, 17), (63, 3, 2), (1000, 7, 3), (2, 2, 2), (64, 4, 16), (64, 4, 17),
+          (200, 9, 33), (3, 300, 5)]
+
+
+@pytest.mark.parametrize("dims", RAGGED, ids=lambda d: "x".join(map(str, d)))
+@pytest.mark.parametrize("idx", [0, 4])
+def test_ragged_shapes_all_variants(tvf, dims, idx):
+    b, p0, r0 = phantoms.make_inputs(idx, dims)
+    lam = phantoms.workload(idx)["lam"]
+    exp = oracle_solve(b, p0, r0, lam, 2, 5)
+    for variant in VARIANTS:
+        got = gpu_solve(tvf, b, p0, r0, lam, 2, 5, variant)
+        label = "%s %s w%d" % (variant, dims, idx)
+        assert_close(got, exp, label)
+        assert_bitwise(got, exp, label)
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_r_different_from_p(tvf, variant):
+    """A mid-run state: r is not p (arbitrary admissible fields)."""
+    dims = (70, 13, 21)
+    b = phantoms.make_b(2, dims)
+    p0 = phantoms.random_ball_field(dims, seed=7)
+    r0 = phantoms.random_ball_field(dims, seed=8)
+    exp = oracle_solve(b, p0, r0, 0.002, 3, 4)
+    got = gpu_solve(tvf, b, p0, r0, 0.002, 3, 4, variant)
+    assert_close(got, exp, "r != p " + variant)
+    assert_bitwise(got, exp, "r != p " + variant)
+
+
+def test_single_step_with_explicit_momentum(tvf):
+    dims = (77, 19, 11)
+    b, p0, r0 = phantoms.make_inputs(4, dims)
+    m = np.float32(0.61803)
+    pe, re = oracle.step(b, p0, r0, 0.003, m)
+    dev = torch.device("cuda")
+    bt = torch.from_numpy(b).to(dev)
+    for variant in VARIANTS:
+        v = tvf.VARIANTS[variant]
+        p = torch.from_numpy(p0).to(dev)
+        ri = torch.from_numpy(r0).to(dev)
+        ro = torch.empty_like(ri)
+        ws = torch.empty_like(bt) if v == tvf.TWO_KERNEL else None
+        tvf.tv_fgp_step(bt, p, ri, ro, 0.003, float(m), variant=v, z_ws=ws)
+        torch.cuda.synchronize()
+        got = (p.cpu().numpy(), ro.cpu().numpy(), oracle.primal(b, p.cpu().numpy(), 0.003))
+        exp = (pe, re, oracle.primal(b, pe, 0.003))
+        assert_bitwise(got, exp, "single step " + variant)
+        assert np.array_equal(ri.cpu().numpy(), r0), "r_in was modified"
+
+
+# --------------------------------------------------------------------------
+# degenerate cases
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_zero_input_stays_zero(tvf, variant):
+    dims = (50, 9, 20)
+    nx, ny, nz = dims
+    b = np.zeros((nz, ny, nx), np.float32)
+    p0 = np.zeros((3, nz, ny, nx), np.float32)
+    p, r, z = gpu_solve(tvf, b, p0, p0, 0.01, 2, 10, variant)
+    for a in (p, r, z):
+        assert not a.any() and not np.signbit(a).any()
+
+
+@pytest.mark.parametrize("c", [0.0, 0.037, -0.2])
+def test_constant_input(tvf, c):
+    dims = (70, 6, 9)
+    nx, ny, nz = dims
+    b = np.full((nz, ny, nx), c, np.float32)
+    p0 = np.zeros((3, nz, ny, nx), np.float32)
+    for variant in VARIANTS:
+        p, r, z = gpu_solve(tvf, b, p0, p0, 0.01, 2, 10, variant)
+        assert not p.any() and not r.any()
+        assert np.array_equal(z, np.full_like(b, max(c, 0.0)))
+
+
+def test_no_steps_leaves_state(tvf):
+    b, p0, r0 = phantoms.make_inputs(4, (40, 10, 6))
+    for no, ni in ((0, 10), (3, 0)):
+        p, r, z = gpu_solve(tvf, b, p0, r0, 0.003, no, ni)
+        assert np.array_equal(p, p0) and np.array_equal(r, r0)
+        assert np.array_equal(z, oracle.primal(b, p0, 0.003))
+
+
+def test_odd_step_count_final_buffer(tvf):
+    b, p0, r0 = phantoms.make_inputs(0, (33, 17, 9))
+    exp = oracle_solve(b, p0, r0, 0.01, 1, 7)
+    got = gpu_solve(tvf, b, p0, r0, 0.01, 1, 7)
+    assert_bitwise(got, exp, "7 steps")
+
+
+def test_non_default_stream(tvf):
+    b, p0, r0, lam, no, ni, exp = reference(0)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        got = gpu_solve(tvf, b, p0, r0, lam, no, ni, "fused", stream=s)
+    assert_bitwise(got, exp, "side stream")
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_nan_guard_bands(tvf, variant):
+    """Buffers sit between NaN guard bands: no write may touch them, no read
+    of them may reach a result."""
+    dims = (67, 9, 18)
+    nx, ny, nz = dims
+    n = nx * ny * nz
+    guard = 4096
+    b, p0, r0 = phantoms.make_inputs(4, dims)
+    exp = oracle_solve(b, p0, r0, 0.003, 1, 6)
+    dev = torch.device("cuda")
+    v = tvf.VARIANTS[variant]
+    store = torch.full((11, n + 2 * guard), float("nan"), device=dev)
+
+    def vol(k, init=None):
+        t = store[k, guard:guard + n].view(nz, ny, nx)
+        if init is not None:
+            t.copy_(torch.from_numpy(np.ascontiguousarray(init)))
+        return t
+
+    bt = vol(0, b)
+    p = [vol(1 + a, p0[a]) for a in range(3)]
+    ra = [vol(4 + a, r0[a]) for a in range(3)]
+    rb = [vol(7 + a) for a in range(3)]
+    ws = vol(10) if v == tvf.TWO_KERNEL else None
+    where = tvf.tv_fgp_run(bt, p, ra, rb, 0.003, 1, 6, variant=v, z_ws=ws)
+    torch.cuda.synchronize()
+    r = rb if where else ra
+    got_p = np.stack([t.cpu().numpy() for t in p])
+    got_r = np.stack([t.cpu().numpy() for t in r])
+    host = store.cpu().numpy()
+    assert np.isnan(host[:, :guard]).all() and np.isnan(host[:, guard + n:]).all()
+    assert_bitwise((got_p, got_r, oracle.primal(b, got_p, 0.003)), exp, "guard " + variant)
+
+
+# --------------------------------------------------------------------------
+# full-size workloads in the launch configuration the bench times
+
+def test_workload2_256_full_200_steps(tvf):
+    b, p0, r0, lam, no, ni, exp = reference(2)
+    got = gpu_solve(tvf, b, p0, r0, lam, no, ni, "fused")
+    assert_close(got, exp, "ellipsoids 256^3")
+    assert_bitwise(got, exp, "ellipsoids 256^3")
+
+
+def test_workload2_256_variants_agree(tvf):
+    b, p0, r0, lam, no, ni, exp = reference(2)
+    for variant in ("two_kernel", "lds_march"):
+        got = gpu_solve(tvf, b, p0, r0, lam, no, ni, variant)
+        assert_bitwise(got, exp, "ellipsoids 256^3 " + variant)
+
+
+def test_workload3_512_full_200_steps(tvf):
+    """The headline volume: all 134M voxels after the full 20 x 10 steps."""
+    b, p0, r0, lam, no, ni, exp = reference(3)
+    got = gpu_solve(tvf, b, p0, r0, lam, no, ni, "fused")
+    assert_close(got, exp, "ellipsoids 512^3")
+    assert_bitwise(got, exp, "ellipsoids 512^3")
+    _cache.clear()
+
+
+def sample_points(dims, rng, n_random):
+    nx, ny, nz = dims
+    pts = set()
+    for z in (0, nz - 1):
+        for y in (0, ny - 1):
+            for x in (0, nx - 1):
+                pts.add((z, y, x))
+    pts |= {(nz // 2, ny // 2, nx - 1), (nz - 1, ny // 2, nx // 2), (nz // 2, 0, nx // 2),
+            (15, 3, 63), (16, 4, 64), (17, 5, 65), (nz - 2, ny - 2, nx - 2)}
+    for _ in range(n_random):
+        pts.add((int(rng.integers(nz)), int(rng.integers(ny)), int(rng.integers(nx))))
+    return sorted(pts)
+
+
+def test_workload4_anisotropic_sampled(tvf):
+    """1000 x 777 x 301: one outer iteration (10 steps), then the full 200.
+
+    After K steps a voxel depends only on inputs within K voxels of it, so
+    the oracle computes sampled voxels from sub-boxes of the inputs.  After
+    200 steps: the corner samples against the oracle, and the properties that
+    hold at every voxel (finite, |p| <= 1, upper-face slots zero).
+    """
+    dims = (1000, 777, 301)
+    nx, ny, nz = dims
+    w = phantoms.workload(4)
+    lam = w["lam"]
+    b, p0, r0 = phantoms.make_inputs(4, dims)
+    rng = np.random.default_rng(4)
+    p10, r10, z10 = gpu_solve(tvf, b, p0, r0, lam, 1, 10, "fused")
+    for c in sample_points(dims, rng, 24):
+        pe, re, ze = oracle.run_cone(b, p0, r0, lam, 1, 10, c)
+        idx = (slice(None),) + c
+        assert np.array_equal(p10[idx].view(np.uint32), pe.view(np.uint32)), c
+        assert np.array_equal(r10[idx].view(np.uint32), re.view(np.uint32)), c
+        assert z10[c] == ze, c
+    del p10, r10, z10
+    p, r, z = gpu_solve(tvf, b, p0, r0, lam, w["n_outer"], w["n_inner"], "fused")
+    for c in [(0, 0, 0), (nz - 1, ny - 1, nx - 1)]:
+        pe, re, ze = oracle.run_cone(b, p0, r0, lam, w["n_outer"], w["n_inner"], c)
+        idx = (slice(None),) + c
+        assert max_abs(p[idx], pe) <= TOL and max_abs(r[idx], re) <= TOL
+        assert abs(float(z[c]) - float(ze)) <= TOL
+        assert np.array_equal(p[idx].view(np.uint32), pe.view(np.uint32)), c
+    assert np.isfinite(p).all() and np.isfinite(r).all() and np.isfinite(z).all()
+    norm = np.sqrt((p.astype(np.float64) ** 2).sum(axis=0))
+    assert norm.max() <= 1.0 + 5e-7
+    assert not p[0, :, :, nx - 1].any() and not p[1, :, ny - 1, :].any()
+    assert not p[2, nz - 1].any()
+    assert (z >= 0).all()
