@@ -41,12 +41,19 @@ class TvFgpError(RuntimeError):
 
 
 def _load():
+    # torch ships its own HIP runtime.  Import it first so that the library's
+    # dependency on libamdhip64.so.7 resolves (by SONAME) to the runtime torch
+    # already loaded; loading the library first would bring a second HIP and
+    # HSA runtime into the process, and torch's streams and allocations would
+    # then be handed to a runtime that does not know them.
+    import torch  # noqa: F401
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             "libtvfgp.so is not built (expected at %s); run "
             "`python -c 'import __graft_entry__ as g; g.build()'` or "
             "`python stencil_dual_update_amd/build_lib.py`" % LIB_PATH)
     lib = ctypes.CDLL(LIB_PATH)
+    _check_single_runtime()
     P = ctypes.c_void_p
     P3 = ctypes.POINTER(ctypes.c_void_p)  # float *const x[3]; NULL allowed
     I64 = ctypes.c_int64
@@ -71,6 +78,19 @@ def _load():
     lib.tv_fgp_variant_name.restype = ctypes.c_char_p
     lib.tv_fgp_variant_name.argtypes = [ctypes.c_int]
     return lib
+
+
+def _check_single_runtime():
+    """Fail loudly if two different HIP runtimes are mapped into the process."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return
+    real = {os.path.realpath(p) for p in paths if p.startswith("/")}
+    if len(real) > 1:
+        raise ImportError("two HIP runtimes are loaded (%s); import torch before "
+                          "loading libtvfgp.so" % ", ".join(sorted(real)))
 
 
 lib = _load()
