@@ -12,9 +12,10 @@ Besides the headline ms/step it reports:
                 p (3); write p (3), r (3)) over the average launch duration,
                 timed with events around every launch on the launch stream,
                 against MI355X's 8 TB/s HBM peak; `traffic` is the HBM bytes
-                per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE summary
+                per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE record
                 committed under profiles/ (null when the kernel sources have
-                changed since those counters were taken)
+                changed since those counters were taken); `bench.py --traffic`
+                builds that record from the two counter runs
   copy          bandwidth of a plain device copy of 2 x 1 GiB on the same box
   cpu_baseline  the CPU oracle (fp32, OpenMP) timed on the host cores on a
                 bounded sample: the first 10 outer iterations (100 steps) of
@@ -29,7 +30,8 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
-BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "two_kernel": 72}
+BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "reg_march": 52,
+                   "two_kernel": 72}
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_512.json")
 METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
 
@@ -54,6 +56,53 @@ def measured_traffic(variant, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def _counter_rows(path):
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = rows.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "grid": r["Grid_Size"],
+                                                   "value": 0.0})
+            d["value"] += float(r["Counter_Value"])
+    return list(rows.values())
+
+
+def write_traffic(fetch_csv, write_csv, out=TRAFFIC_FILE):
+    """Turn two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE,
+    KiB per dispatch) into the per-launch HBM traffic of the fused kernel.
+
+    Each counter is scaled by what it reads for the bench's copy probe, a
+    device copy of exactly 1 GiB read + 1 GiB written.
+    """
+    import statistics
+    res = {}
+    for key, path in (("fetch", fetch_csv), ("write", write_csv)):
+        rows = _counter_rows(path)
+        copy = [r["value"] for r in rows if "copyBuffer" in r["name"]]
+        fused = [r["value"] for r in rows if "fused_zx_kernel" in r["name"]]
+        if not copy or not fused:
+            raise SystemExit("%s: no copy or fused dispatches found" % path)
+        copy_kib = statistics.median(copy)
+        scale = (1 << 20) / copy_kib          # KiB of 1 GiB / counter reading
+        res[key] = {"kernel_kib_median": statistics.median(fused),
+                    "copy_kib_median": copy_kib, "scale": scale,
+                    "dispatches": len(fused)}
+    fetch_b = res["fetch"]["kernel_kib_median"] * res["fetch"]["scale"] * 1024
+    write_b = res["write"]["kernel_kib_median"] * res["write"]["scale"] * 1024
+    vol = 512 ** 3 * 4
+    rec = {"kernel": "fused_zx_kernel", "workload": "ellipsoids 512^3",
+           "kernel_source_sha256": kernel_source_digest(),
+           "fetch": res["fetch"], "write": res["write"],
+           "hbm_read_bytes_per_launch": round(fetch_b),
+           "hbm_write_bytes_per_launch": round(write_b),
+           "hbm_bytes_per_launch": round(fetch_b + write_b),
+           "volumes_read": round(fetch_b / vol, 3), "volumes_written": round(write_b / vol, 3),
+           "algorithmic_bytes_per_launch": 52 * 512 ** 3}
+    with open(out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -61,15 +110,21 @@ def parse():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--variant", default="fused",
-                    choices=["fused", "lds_march", "two_kernel", "point"])
+                    choices=sorted(BYTES_PER_VOXEL))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy probe")
+    ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: build the traffic record under profiles/ from "
+                         "two rocprofv3 --pmc counter_collection.csv files of this bench")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.traffic:
+        write_traffic(*args.traffic)
+        return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(the step would shard by z-slabs with a one-plane halo; not built). "

@@ -56,14 +56,18 @@ extern "C" {
 #define TV_ERR_ALIGN     -8  /* a pointer is not 4-byte aligned                       */
 
 /* Kernel variants.  All give bit-identical results. */
-#define TV_FGP_FUSED      0  /* default: one fused pass; each thread walks a column
-                                along z and carries z and r between planes           */
-#define TV_FGP_LDS_MARCH  1  /* ablation: an x-y tile marches along z with the
-                                planes of r and z staged in LDS                      */
+#define TV_FGP_FUSED      0  /* default: one fused pass; 64x8 x-y tiles march along
+                                z, z is computed once per point and exchanged
+                                through LDS, r is read through the caches            */
+#define TV_FGP_LDS_MARCH  1  /* ablation: 64x4 x-y tiles march along z with two
+                                planes of z in LDS and two barriers per plane        */
 #define TV_FGP_TWO_KERNEL 2  /* ablation: a primal kernel writes z to the workspace,
                                 a dual kernel reads it (18 volumes per step)         */
 #define TV_FGP_POINT      3  /* ablation: one voxel per thread, z recomputed at the
                                 voxel and its three upper neighbours                 */
+#define TV_FGP_REG_MARCH  4  /* ablation: each thread walks a column along z,
+                                carries its own z and r in registers and recomputes
+                                z at the +x and +y neighbours                        */
 
 /*
  * One FGP step ("TV solver: the FGP step on the GPU", section "What one step
@@ -144,7 +148,8 @@ float tv_fgp_momentum(int k);
 /* Static, NUL-terminated description of a status code. */
 const char *tv_fgp_status_string(int status);
 
-/* Name of a variant ("fused", "lds_march", "two_kernel", "point"), or NULL. */
+/* Name of a variant ("fused", "lds_march", "two_kernel", "point",
+   "reg_march"), or NULL. */
 const char *tv_fgp_variant_name(int variant);
 
 #ifdef __cplusplus

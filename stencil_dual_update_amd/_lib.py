@@ -25,8 +25,9 @@ FUSED = 0
 LDS_MARCH = 1
 TWO_KERNEL = 2
 POINT = 3
+REG_MARCH = 4
 VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
-            "point": POINT}
+            "point": POINT, "reg_march": REG_MARCH}
 
 # Names declared in include/tv_fgp.h, in declaration order.
 EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_primal",

@@ -244,6 +244,7 @@ const char *tv_fgp_variant_name(int variant) {
     case tvfgp::kVariantLdsMarch: return "lds_march";
     case tvfgp::kVariantTwoKernel: return "two_kernel";
     case tvfgp::kVariantPoint: return "point";
+    case tvfgp::kVariantRegMarch: return "reg_march";
     default: return nullptr;
   }
 }

@@ -1,4 +1,5 @@
-// HIP kernels of the FGP step for gfx950 (MI355X) and their launchers.
+// Ablation kernels of the FGP step for gfx950 (MI355X) and the dispatch of
+// all variants.  The default kernel is in tv_fgp_fused.hip.
 //
 // The step ("TV solver: the FGP step on the GPU", section "What one step
 // does") is bound by HBM traffic: per voxel it must read b, r (3) and p (3)
@@ -25,7 +26,7 @@ namespace tvfgp {
 namespace {
 
 // --------------------------------------------------------------------------
-// Default: fused pass with a register march along z.
+// Ablation: fused pass with a register march along z.
 //
 // Each thread owns the column (x, y) of a tile for `planes` consecutive z.
 // At plane z it needs z(i), z(i+e_x), z(i+e_y), z(i+e_z).  z(i+e_z) computed
@@ -281,7 +282,9 @@ int launch_step_t(const StepArgs &a) {
   hipStream_t s = (hipStream_t)a.stream;
   const dim3 block(kBlock);
   switch (a.variant) {
-    case kVariantFused: {
+    case kVariantFused:
+      return launch_fused_zx(a);
+    case kVariantRegMarch: {
       const Geometry<I> g = make_geometry<I>(a.nx, a.ny, a.nz, a.planes);
       fused_march_kernel<I><<<grid_for(g.ntiles), block, 0, s>>>(
           a.b, a.p[0], a.p[1], a.p[2], a.r_in[0], a.r_in[1], a.r_in[2],

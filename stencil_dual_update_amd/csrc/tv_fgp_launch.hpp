@@ -12,12 +12,14 @@ constexpr int kVariantFused = 0;
 constexpr int kVariantLdsMarch = 1;
 constexpr int kVariantTwoKernel = 2;
 constexpr int kVariantPoint = 3;
-constexpr int kNumVariants = 4;
+constexpr int kVariantRegMarch = 4;
+constexpr int kNumVariants = 5;
 
 constexpr int kLaunchFailed = -1;
 
-// Planes along z that one thread (or one tile) walks in the marching kernels.
-constexpr int64_t kDefaultPlanes = 16;
+// Planes along z that one thread (or one tile) walks in the marching
+// ablation kernels (the default kernel fixes its own tile shape).
+constexpr int64_t kDefaultPlanes = 8;
 
 struct StepArgs {
   const float *b;
@@ -49,8 +51,11 @@ struct PrimalArgs {
 int launch_step(const StepArgs &a);
 int launch_primal(const PrimalArgs &a);
 int launch_lds_march(const StepArgs &a);
+int launch_fused_zx(const StepArgs &a);
 
-// True when every index the kernels form at these dimensions fits in int32.
+// True when every index the ablation kernels form fits in int32.
 bool fits_int32(int64_t nx, int64_t ny, int64_t nz);
+// True when every byte offset the default kernel forms fits in 32 bits.
+bool fits_u32_offsets(int64_t nx, int64_t ny, int64_t nz);
 
 }  // namespace tvfgp

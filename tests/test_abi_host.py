@@ -86,7 +86,7 @@ def test_variant_names():
 
 def test_workspace_bytes():
     assert tvf.workspace_bytes(tvf.TWO_KERNEL, 10, 20, 30) == 10 * 20 * 30 * 4
-    for v in (tvf.FUSED, tvf.LDS_MARCH, tvf.POINT):
+    for v in (tvf.FUSED, tvf.LDS_MARCH, tvf.POINT, tvf.REG_MARCH):
         assert tvf.workspace_bytes(v, 10, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.TWO_KERNEL, 0, 20, 30) == 0
     assert tvf.workspace_bytes(7, 10, 20, 30) == 0
@@ -117,7 +117,7 @@ def test_workspace_bytes():
     (dict(lam=1e-45), tvf.TV_ERR_PARAM),           # 1/(12 lambda) overflows
     (dict(m=float("nan")), tvf.TV_ERR_PARAM),
     (dict(m=float("inf")), tvf.TV_ERR_PARAM),
-    (dict(variant=4), tvf.TV_ERR_VARIANT),
+    (dict(variant=5), tvf.TV_ERR_VARIANT),
     (dict(variant=-1), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),       # two-kernel without z
     (dict(variant=2, ws=0), tvf.TV_ERR_ALIAS),     # workspace aliases b

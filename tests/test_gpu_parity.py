@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
-VARIANTS = ["fused", "lds_march", "two_kernel", "point"]
+VARIANTS = ["fused", "lds_march", "two_kernel", "point", "reg_march"]
 
 
 @pytest.fixture(scope="module")
