@@ -109,6 +109,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--dims", type=int, nargs=3, metavar=("NX", "NY", "NZ"),
+                    help="run the workload's recipe at other dimensions")
     ap.add_argument("--variant", default="fused",
                     choices=sorted(BYTES_PER_VOXEL))
     ap.add_argument("--no-cpu-baseline", action="store_true",
@@ -140,14 +142,14 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     w = phantoms.workload(args.workload)
-    nx, ny, nz = w["dims"]
+    nx, ny, nz = args.dims or w["dims"]
     lam = w["lam"]
     n_inner = w["n_inner"]
     variant = tvf.VARIANTS[args.variant]
     nvox = nx * ny * nz
 
     t0 = time.time()
-    b_host, p0_host, _ = phantoms.make_inputs(args.workload)
+    b_host, p0_host, _ = phantoms.make_inputs(args.workload, (nx, ny, nz))
     gen_s = time.time() - t0
     b = torch.from_numpy(b_host).to(dev)
     p = torch.from_numpy(p0_host).to(dev)
@@ -238,7 +240,7 @@ def main():
                          "full size, fp32 exact-order oracle, %.1f s" % (
                              cpu_outer, cpu_steps, cpu_s)}
 
-    traffic = measured_traffic(args.variant, args.workload)
+    traffic = None if args.dims else measured_traffic(args.variant, args.workload)
     out = {
         "metric": METRIC,
         "value": round(ms_per_step, 5),
@@ -252,7 +254,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": phantoms.NAMES[args.workload],
+        "config": {"workload": phantoms.NAMES[args.workload] if not args.dims else
+                   "%s recipe at %dx%dx%d" % (phantoms.NAMES[args.workload], nx, ny, nz),
                    "dims": [nx, ny, nz], "lambda": lam, "steps_per_outer": n_inner,
                    "variant": args.variant, "parallelism": "single GPU"},
         "gbps": round(region_gbs, 1),

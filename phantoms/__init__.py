@@ -140,6 +140,19 @@ def random_ball_field(dims, seed):
     return out
 
 
+def make_uniform(dims, seed, lo, hi):
+    """float32 volume (nz, ny, nx) of independent U[lo, hi) draws, drawn in float32."""
+    nx, ny, nz = dims
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.empty((nz, ny, nx), dtype=np.float32)
+    for z0 in range(0, nz, _SLAB):
+        z1 = min(z0 + _SLAB, nz)
+        out[z0:z1] = rng.random(size=(z1 - z0, ny, nx), dtype=np.float32)
+    out *= np.float32(hi - lo)
+    out += np.float32(lo)
+    return out
+
+
 def make_p0(idx, dims=None):
     """Initial dual p of workload ``idx`` (float32, (3, nz, ny, nx)); r starts equal."""
     w = WORKLOADS[idx]

@@ -17,11 +17,16 @@
 //     their latency overlaps the barrier and the dual update;
 //   - p is read and p, r_out are written with non-temporal hints (touched once
 //     per step), which keeps L2 for the r and b neighbour reuse;
-//   - tiles are ordered x fastest, then y within a band of kBand tile rows,
-//     then z, then band, and each XCD takes a contiguous range: the tile above
-//     in z runs a few dozen tiles later on the same XCD, so the plane it
-//     shares with this tile is still in that XCD's L2.  Measured on MI355X
-//     this brings the HBM reads to within ~1% of the 7 compulsory volumes.
+//   - tiles are ordered x fastest within a group of up to 16 tile columns,
+//     then y within a band of rows, then z, then band, then group, and each
+//     XCD takes a contiguous range.  Group width x band height is about 64
+//     tiles, the number of tiles whose reads fit in one XCD's 4 MB L2, so the
+//     tile above in z runs about 64 tiles later on the same XCD and finds the
+//     plane it shares with this tile still in L2.  Measured on MI355X this
+//     brings the HBM reads to within ~1% of the 7 compulsory volumes at 512^3;
+//   - p is read with a streaming hint only when rows start on 128-byte
+//     cache-line boundaries: with misaligned rows a streaming load makes the
+//     two tiles sharing a line fetch it twice.
 // Addresses are 32-bit byte offsets from the volume base (one scalar base and
 // one vector offset per load) when every offset fits; otherwise 64-bit.
 #include <hip/hip_runtime.h>
@@ -41,7 +46,8 @@ constexpr int kZxTileX = 64;  // one wave64 per tile row
 constexpr int kZxTileY = 8;   // rows per tile (8 waves, 512 threads)
 constexpr int kZxBlock = kZxTileX * kZxTileY;
 constexpr int kZxPlanes = 4;  // z planes per tile
-constexpr int kZxBand = 8;    // tile rows per band in the tile order
+constexpr int kZxGroupMax = 16;  // tile columns per group in the tile order
+constexpr int kZxReach = 64;     // tiles whose reads one XCD's L2 holds
 
 template <typename I, typename Off>
 struct ZxGeometry {
@@ -50,7 +56,8 @@ struct ZxGeometry {
   I tiles_x, tiles_y, tiles_z;
   I ntiles;
   I planes;
-  I band;
+  I group;  // tile columns per group
+  I band;   // tile rows per band
 };
 
 template <typename Off>
@@ -70,22 +77,29 @@ __device__ __forceinline__ void st_stream(float *__restrict__ base, Off off,
   __builtin_nontemporal_store(v, (float *)((char *)base + off));
 }
 
-// Tile t (after the XCD mapping) -> (tx, ty, tz) in band order.
-template <typename I>
-__device__ __forceinline__ void band_tile(I tile, I tiles_x, I tiles_y,
-                                          I tiles_z, I band, I &tx, I &ty,
-                                          I &tz) {
-  tx = tile % tiles_x;
-  const I pair = tile / tiles_x;  // index over (ty, tz)
-  const I per_band = band * tiles_z;
-  const I bnd = pair / per_band;
-  const I in_band = pair % per_band;
-  const I rows = (tiles_y - bnd * band < band) ? tiles_y - bnd * band : band;
-  tz = in_band / rows;
-  ty = bnd * band + in_band % rows;
+// Tile t (after the XCD mapping) -> (tx, ty, tz).  Order, slowest first:
+// group of tile columns, band of tile rows, z, row within the band, column
+// within the group.  The last group and the last band may be narrower.
+template <typename I, typename Off>
+__device__ __forceinline__ void ordered_tile(I t, const ZxGeometry<I, Off> &g,
+                                             I &tx, I &ty, I &tz) {
+  const I per_group = g.group * g.tiles_y * g.tiles_z;
+  const I grp = t / per_group;
+  I rem = t % per_group;
+  const I x_lo = grp * g.group;
+  const I width = (g.tiles_x - x_lo < g.group) ? g.tiles_x - x_lo : g.group;
+  const I per_band = width * g.band * g.tiles_z;
+  const I bnd = rem / per_band;
+  rem = rem % per_band;
+  const I y_lo = bnd * g.band;
+  const I height = (g.tiles_y - y_lo < g.band) ? g.tiles_y - y_lo : g.band;
+  tz = rem / (width * height);
+  rem = rem % (width * height);
+  ty = y_lo + rem / width;
+  tx = x_lo + rem % width;
 }
 
-template <typename I, typename Off>
+template <typename I, typename Off, bool kStreamP>
 __global__ __launch_bounds__(kZxBlock) void fused_zx_kernel(
     const float *__restrict__ b, float *__restrict__ p0,
     float *__restrict__ p1, float *__restrict__ p2,
@@ -112,8 +126,7 @@ __global__ __launch_bounds__(kZxBlock) void fused_zx_kernel(
 
   for (I t = (I)blockIdx.x; t < g.ntiles; t += (I)gridDim.x) {
     I tx, ty, tz;
-    band_tile<I>(xcd_tile(t, g.ntiles), g.tiles_x, g.tiles_y, g.tiles_z,
-                 g.band, tx, ty, tz);
+    ordered_tile<I, Off>(xcd_tile(t, g.ntiles), g, tx, ty, tz);
     const I x0 = tx * kZxTileX, y0 = ty * kZxTileY;
     const I z0 = tz * g.planes;
     const I z1 = (z0 + g.planes < g.nz) ? z0 + g.planes : g.nz;
@@ -185,9 +198,9 @@ __global__ __launch_bounds__(kZxBlock) void fused_zx_kernel(
       const Off ok = oi + (Off)(k - z0) * sz4;
       float pv0 = 0.0f, pv1 = 0.0f, pv2 = 0.0f;
       if (own_ok) {
-        pv0 = ld_stream(p0, ok);
-        pv1 = ld_stream(p1, ok);
-        pv2 = ld_stream(p2, ok);
+        pv0 = kStreamP ? ld_stream(p0, ok) : ld(p0, ok);
+        pv1 = kStreamP ? ld_stream(p1, ok) : ld(p1, ok);
+        pv2 = kStreamP ? ld_stream(p2, ok) : ld(p2, ok);
       }
       // plane k+1 values in hand; start the loads of plane k+2
       const float cb = nb, c0 = n0, c1 = n1, c2 = n2, c0l = n0l, c1l = n1l;
@@ -246,17 +259,33 @@ ZxGeometry<I, Off> zx_geometry(int64_t nx, int64_t ny, int64_t nz) {
   g.planes = (I)kZxPlanes;
   g.tiles_z = (I)((nz + kZxPlanes - 1) / kZxPlanes);
   g.ntiles = g.tiles_x * g.tiles_y * g.tiles_z;
-  g.band = (I)kZxBand;
+  g.group = g.tiles_x < (I)kZxGroupMax ? g.tiles_x : (I)kZxGroupMax;
+  const I band = (I)kZxReach / g.group;
+  g.band = band < 1 ? 1 : (band > 16 ? 16 : band);
   return g;
+}
+
+// Rows (and therefore planes) of p start on 128-byte boundaries.
+inline bool rows_line_aligned(const StepArgs &a) {
+  if ((a.nx * 4) % 128 != 0) return false;
+  for (int k = 0; k < 3; ++k)
+    if (((uintptr_t)a.p[k]) % 128 != 0) return false;
+  return true;
 }
 
 template <typename I, typename Off>
 int launch_zx(const StepArgs &a) {
   const ZxGeometry<I, Off> g = zx_geometry<I, Off>(a.nx, a.ny, a.nz);
-  fused_zx_kernel<I, Off><<<grid_for(g.ntiles), dim3(kZxBlock), 0,
-                            (hipStream_t)a.stream>>>(
-      a.b, a.p[0], a.p[1], a.p[2], a.r_in[0], a.r_in[1], a.r_in[2],
-      a.r_out[0], a.r_out[1], a.r_out[2], a.lam, a.c, a.m, g);
+  const dim3 grid(grid_for(g.ntiles)), block(kZxBlock);
+  hipStream_t s = (hipStream_t)a.stream;
+  if (rows_line_aligned(a))
+    fused_zx_kernel<I, Off, true><<<grid, block, 0, s>>>(
+        a.b, a.p[0], a.p[1], a.p[2], a.r_in[0], a.r_in[1], a.r_in[2],
+        a.r_out[0], a.r_out[1], a.r_out[2], a.lam, a.c, a.m, g);
+  else
+    fused_zx_kernel<I, Off, false><<<grid, block, 0, s>>>(
+        a.b, a.p[0], a.p[1], a.p[2], a.r_in[0], a.r_in[1], a.r_in[2],
+        a.r_out[0], a.r_out[1], a.r_out[2], a.lam, a.c, a.m, g);
   return hipGetLastError() == hipSuccess ? 0 : kLaunchFailed;
 }
 

@@ -1,0 +1,69 @@
+"""GPU parity on a volume past 2^31 voxels (64-bit offset and index paths).
+
+1400 x 1300 x 1200 = 2.18e9 voxels, 8.7 GB per volume.  At this size the
+default kernel switches from 32-bit to 64-bit byte offsets, the ablation
+kernels from int32 to int64 indices, and the grid is smaller than the tile
+count, so workgroups loop over tiles.  Each variant runs two steps; sampled
+voxels (corners, faces, interior, tile and group edges) are compared with the
+CPU oracle on sub-boxes of the inputs (after K steps a voxel depends only on
+inputs within K voxels of it).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import phantoms
+
+torch = pytest.importorskip("torch")
+
+pytestmark = pytest.mark.gpu
+
+DIMS = (1400, 1300, 1200)
+LAM = 0.01
+
+
+def test_volume_past_2_31_voxels_all_variants():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import stencil_dual_update_amd as tvf
+    nx, ny, nz = DIMS
+    n = nx * ny * nz
+    assert n > 2 ** 31
+    free, _ = torch.cuda.mem_get_info()
+    need = 12 * n * 4
+    assert free > need, "needs %.0f GB of device memory, %.0f GB free" % (need / 1e9, free / 1e9)
+    b = phantoms.make_uniform(DIMS, seed=11, lo=-0.01, hi=0.05)
+    dev = torch.device("cuda")
+    bt = torch.from_numpy(b).to(dev)
+    p = torch.empty((3, nz, ny, nx), device=dev)
+    ra = torch.empty_like(p)
+    rb = torch.empty_like(p)
+    ws = torch.empty_like(bt)
+    pts = [(0, 0, 0), (nz - 1, ny - 1, nx - 1), (nz // 2, ny // 2, nx // 2), (7, 1299, 0),
+           (1199, 0, 1399), (600, 8 * 81, 64 * 16), (601, 8 * 81 - 1, 64 * 16 - 1),
+           (1100, 517, 1023), (3, 4, 1024), (1196, 1297, 700)]
+    expected = {}
+    for c in pts:
+        lo = [max(v - 3, 0) for v in c]
+        hi = [min(v + 4, s) for v, s in zip(c, (nz, ny, nx))]
+        sub = np.ascontiguousarray(b[lo[0]:hi[0], lo[1]:hi[1], lo[2]:hi[2]])
+        p0 = np.zeros((3,) + sub.shape, np.float32)
+        pe, re, ze = oracle.run_cone(sub, p0, p0, LAM, 1, 2,
+                                     (c[0] - lo[0], c[1] - lo[1], c[2] - lo[2]))
+        expected[c] = (pe, re, ze)
+    for variant, v in tvf.VARIANTS.items():
+        p.zero_()
+        ra.zero_()
+        where = tvf.tv_fgp_run(bt, p, ra, rb, LAM, 1, 2, variant=v,
+                               z_ws=ws if v == tvf.TWO_KERNEL else None)
+        r = rb if where else ra
+        tvf.tv_primal(bt, p, ws, LAM)
+        torch.cuda.synchronize()
+        for c, (pe, re, ze) in expected.items():
+            gp = p[:, c[0], c[1], c[2]].cpu().numpy()
+            gr = r[:, c[0], c[1], c[2]].cpu().numpy()
+            gz = ws[c].item()
+            assert np.array_equal(gp.view(np.uint32), pe.view(np.uint32)), (variant, c, gp, pe)
+            assert np.array_equal(gr.view(np.uint32), re.view(np.uint32)), (variant, c, gr, re)
+            assert np.float32(gz) == ze, (variant, c, gz, ze)
+    del bt, p, ra, rb, ws
+    torch.cuda.empty_cache()

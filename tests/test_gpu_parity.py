@@ -109,7 +109,7 @@ def test_workload1_blobs_128_full_200_steps(tvf, variant):
 
 RAGGED = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70),
           (65, 5, 17), (63, 3, 2), (1000, 7, 3), (2, 2, 2), (64, 4, 16), (64, 4, 17),
-          (200, 9, 33), (3, 300, 5)]
+          (200, 9, 33), (3, 300, 5), (1100, 10, 6), (64, 70, 10), (2100, 20, 5)]
 
 
 @pytest.mark.parametrize("dims", RAGGED, ids=lambda d: "x".join(map(str, d)))
