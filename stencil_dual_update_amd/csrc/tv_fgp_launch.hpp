@@ -53,9 +53,4 @@ int launch_primal(const PrimalArgs &a);
 int launch_lds_march(const StepArgs &a);
 int launch_fused_zx(const StepArgs &a);
 
-// True when every index the ablation kernels form fits in int32.
-bool fits_int32(int64_t nx, int64_t ny, int64_t nz);
-// True when every byte offset the default kernel forms fits in 32 bits.
-bool fits_u32_offsets(int64_t nx, int64_t ny, int64_t nz);
-
 }  // namespace tvfgp

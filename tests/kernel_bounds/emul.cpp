@@ -1,0 +1,170 @@
+// CPU bounds check of the HIP kernel sources (test infrastructure).
+//
+// The kernel headers are compiled as host C++ (see shim/hip/hip_runtime.h)
+// and every thread of every workgroup of a launch is run one after another
+// on buffers that sit flush against inaccessible guard regions of 8 GiB on
+// each side.  Any read or write outside a buffer -- including a 32-bit
+// offset that wrapped below zero -- lands in a guard region and raises
+// SIGSEGV; the caller treats a non-zero exit as a failure.  Results are not
+// checked here (barriers are no-ops), only addresses.
+//
+// usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
+//   variant: fused | fused_nostream | reg_march | point | two_kernel | lds_march | primal
+//   wide: 1 instantiates the 64-bit offset / index path regardless of size
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#include <sys/mman.h>
+
+#include "tv_fgp_ablation_kernels.hpp"
+#include "tv_fgp_device.hpp"
+#include "tv_fgp_fused_kernel.hpp"
+#include "tv_fgp_lds_kernel.hpp"
+
+thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
+
+namespace {
+
+const size_t kGuard = size_t(8) << 30;
+
+float *guarded(size_t bytes, bool end_aligned, unsigned seed) {
+  const size_t page = 4096;
+  const size_t span = (bytes + page - 1) / page * page;
+  void *r = mmap(nullptr, kGuard + span + kGuard, PROT_NONE,
+                 MAP_PRIVATE | MAP_ANONYMOUS | MAP_NORESERVE, -1, 0);
+  if (r == MAP_FAILED) {
+    perror("mmap");
+    exit(3);
+  }
+  char *mid = (char *)r + kGuard;
+  if (mprotect(mid, span, PROT_READ | PROT_WRITE) != 0) {
+    perror("mprotect");
+    exit(3);
+  }
+  float *p = end_aligned ? (float *)(mid + span - bytes) : (float *)mid;
+  const size_t n = bytes / sizeof(float);
+  unsigned s = seed * 2654435761u + 1u;
+  for (size_t i = 0; i < n; ++i) {
+    s = s * 1664525u + 1013904223u;
+    p[i] = ((float)(s >> 8) / 16777216.0f - 0.5f) * 0.1f;
+  }
+  return p;
+}
+
+template <typename F>
+void run_grid(unsigned grid, unsigned block, F &&thread_body) {
+  gridDim = {grid, 1, 1};
+  blockDim = {block, 1, 1};
+  for (unsigned bl = 0; bl < grid; ++bl) {
+    for (unsigned th = 0; th < block; ++th) {
+      blockIdx = {bl, 0, 0};
+      threadIdx = {th, 0, 0};
+      thread_body();
+    }
+  }
+}
+
+unsigned pick_grid(int64_t ntiles, unsigned override_grid) {
+  if (override_grid) return override_grid;
+  return tvfgp::grid_for(ntiles);
+}
+
+struct Bufs {
+  float *b, *p[3], *ri[3], *ro[3], *z;
+};
+
+template <typename I, typename Off>
+void run_fused(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid,
+               bool stream_p) {
+  const auto g = tvfgp::zx_geometry<I, Off>(nx, ny, nz);
+  const unsigned gr = pick_grid(g.ntiles, grid);
+  if (stream_p)
+    run_grid(gr, tvfgp::kZxBlock, [&] {
+      tvfgp::fused_zx_kernel<I, Off, true>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1],
+                                           v.ri[2], v.ro[0], v.ro[1], v.ro[2], 0.01f,
+                                           8.3f, 0.5f, g);
+    });
+  else
+    run_grid(gr, tvfgp::kZxBlock, [&] {
+      tvfgp::fused_zx_kernel<I, Off, false>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1],
+                                            v.ri[2], v.ro[0], v.ro[1], v.ro[2], 0.01f,
+                                            8.3f, 0.5f, g);
+    });
+}
+
+template <typename I>
+void run_ablation(const char *variant, const Bufs &v, int64_t nx, int64_t ny, int64_t nz,
+                  unsigned grid, int64_t planes) {
+  using namespace tvfgp;
+  if (!strcmp(variant, "reg_march")) {
+    const Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
+    run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
+      fused_march_kernel<I>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2],
+                            v.ro[0], v.ro[1], v.ro[2], 0.01f, 8.3f, 0.5f, g);
+    });
+  } else if (!strcmp(variant, "point")) {
+    const Geometry<I> g = make_geometry<I>(nx, ny, nz, 1);
+    run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
+      fused_point_kernel<I>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2],
+                            v.ro[0], v.ro[1], v.ro[2], 0.01f, 8.3f, 0.5f, g);
+    });
+  } else if (!strcmp(variant, "two_kernel") || !strcmp(variant, "primal")) {
+    const Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
+    run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
+      primal_kernel<I>(v.b, v.ri[0], v.ri[1], v.ri[2], v.z, 0.01f, g);
+    });
+    if (!strcmp(variant, "two_kernel"))
+      run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
+        dual_kernel<I>(v.z, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2], v.ro[0],
+                       v.ro[1], v.ro[2], 8.3f, 0.5f, g);
+      });
+  } else if (!strcmp(variant, "lds_march")) {
+    const Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
+    run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
+      lds_march_kernel<I>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2], v.ro[0],
+                          v.ro[1], v.ro[2], 0.01f, 8.3f, 0.5f, g);
+    });
+  } else {
+    fprintf(stderr, "unknown variant %s\n", variant);
+    exit(2);
+  }
+}
+
+}  // namespace
+
+int main(int argc, char **argv) {
+  if (argc != 9) {
+    fprintf(stderr, "usage: emul variant nx ny nz wide grid end_aligned planes\n");
+    return 2;
+  }
+  const char *variant = argv[1];
+  const int64_t nx = atoll(argv[2]), ny = atoll(argv[3]), nz = atoll(argv[4]);
+  const bool wide = atoi(argv[5]) != 0;
+  const unsigned grid = (unsigned)atoi(argv[6]);
+  const bool end_aligned = atoi(argv[7]) != 0;
+  const int64_t planes = atoll(argv[8]);
+  const size_t bytes = (size_t)(nx * ny * nz) * sizeof(float);
+  Bufs v;
+  unsigned seed = 1;
+  v.b = guarded(bytes, end_aligned, seed++);
+  for (int a = 0; a < 3; ++a) {
+    v.p[a] = guarded(bytes, end_aligned, seed++);
+    v.ri[a] = guarded(bytes, end_aligned, seed++);
+    v.ro[a] = guarded(bytes, end_aligned, seed++);
+  }
+  v.z = guarded(bytes, end_aligned, seed++);
+  if (!strcmp(variant, "fused") || !strcmp(variant, "fused_nostream")) {
+    const bool sp = !strcmp(variant, "fused");
+    if (wide)
+      run_fused<int64_t, uint64_t>(v, nx, ny, nz, grid, sp);
+    else
+      run_fused<int32_t, uint32_t>(v, nx, ny, nz, grid, sp);
+  } else if (wide) {
+    run_ablation<int64_t>(variant, v, nx, ny, nz, grid, planes);
+  } else {
+    run_ablation<int32_t>(variant, v, nx, ny, nz, grid, planes);
+  }
+  printf("ok %s %lldx%lldx%lld wide=%d grid=%u end=%d planes=%lld\n", variant, (long long)nx,
+         (long long)ny, (long long)nz, (int)wide, grid, (int)end_aligned, (long long)planes);
+  return 0;
+}
