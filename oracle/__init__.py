@@ -53,6 +53,9 @@ def _load():
         f = getattr(lib, "tv_oracle_primal_readout_" + suf)
         f.restype = None
         f.argtypes = [P] * 4 + [real, P, I64, I64, I64]
+        f = getattr(lib, "tv_oracle_duality_gap_" + suf)
+        f.restype = ctypes.c_int
+        f.argtypes = [P] * 4 + [real, I64, I64, I64, P]
     _lib = lib
     return lib
 
@@ -125,6 +128,24 @@ def primal(b, p, lam):
         _ptr(b), _ptr(p[0]), _ptr(p[1]), _ptr(p[2]), real(lam), _ptr(z),
         *_dims(b))
     return z
+
+
+def duality_gap(b, p, lam):
+    """(G, TV(z), 1/2||z - b||^2) for z = max(b - lam L(p), 0), G in per-voxel form.
+
+    G = lam * sum_i (|g(i)| - g(i).p(i)) with g = D z; see tv_fgp_oracle_body.h
+    for why this equals the primal-dual gap P(z) - d(p).  z and g in b's
+    precision, per-voxel terms and sums in double.
+    """
+    b = np.ascontiguousarray(b)
+    suf, real = _suffix(b.dtype)
+    p = np.ascontiguousarray(p, dtype=b.dtype)
+    out = np.zeros(3, dtype=np.float64)
+    rc = getattr(_load(), "tv_oracle_duality_gap_" + suf)(
+        _ptr(b), _ptr(p[0]), _ptr(p[1]), _ptr(p[2]), real(lam), *_dims(b), _ptr(out))
+    if rc != 0:
+        raise MemoryError("oracle duality gap could not allocate scratch")
+    return float(out[0]), float(out[1]), float(out[2])
 
 
 def step(b, p, r, lam, m):

@@ -213,3 +213,51 @@ int FN(tv_oracle_step)(const REAL *b, REAL *p0, REAL *p1, REAL *p2,
     free(zv);
     return 0;
 }
+
+/*
+ * Duality gap of a dual field p, in the per-voxel form
+ *   G(p) = lambda * sum_i ( |g(i)| - g(i).p(i) ),   g = D z,  z = max(b - lambda L(p), 0)
+ * with |.| the Euclidean norm of the 3-vector.  For the problem the FGP step
+ * solves (minimise 1/2||z - b||^2 + lambda sum_i |(Dz)(i)| over z >= 0) the
+ * primal value is P(z) = 1/2||z - b||^2 + lambda sum_i |g(i)| and the dual
+ * value d(p) = 1/2||b||^2 - 1/2||z||^2; because z = max(w, 0) with
+ * w = b - lambda L(p) satisfies z (z - w) = 0 and <z, L p> = <D z, p> for an
+ * admissible p, P(z) - d(p) = <z, z - b> + lambda sum |g| = the form above.
+ * Each term is >= 0 when |p(i)| <= 1, so the sum has no cancellation.
+ * z and g are computed in REAL exactly as the step does; the per-voxel
+ * terms and the sums are in double, without contraction:
+ *   norm = sqrt((gx*gx + gy*gy) + gz*gz),  dot = (gx*px + gy*py) + gz*pz.
+ * out[0] = G, out[1] = sum_i |g(i)| (total variation of z),
+ * out[2] = 1/2 sum_i (z - b)^2.   Returns 0, or -1 if scratch allocation fails.
+ */
+int FN(tv_oracle_duality_gap)(const REAL *b, const REAL *p0, const REAL *p1,
+                              const REAL *p2, REAL lam, int64_t nx, int64_t ny,
+                              int64_t nz, double *out)
+{
+    const int64_t n = nx * ny * nz;
+    REAL *zv = (REAL *)malloc((size_t)n * sizeof(REAL));
+    REAL *g = (REAL *)malloc((size_t)n * 3 * sizeof(REAL));
+    if (!zv || !g) {
+        free(zv);
+        free(g);
+        return -1;
+    }
+    FN(tv_oracle_primal)(b, p0, p1, p2, lam, zv, nx, ny, nz);
+    FN(tv_oracle_D)(zv, g, g + n, g + 2 * n, nx, ny, nz);
+    double sum_gap = 0.0, sum_tv = 0.0, sum_fid = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double gx = (double)g[i], gy = (double)g[n + i], gz = (double)g[2 * n + i];
+        const double norm = sqrt((gx * gx + gy * gy) + gz * gz);
+        const double dot = (gx * (double)p0[i] + gy * (double)p1[i]) + gz * (double)p2[i];
+        const double d = (double)zv[i] - (double)b[i];
+        sum_gap += norm - dot;
+        sum_tv += norm;
+        sum_fid += 0.5 * (d * d);
+    }
+    out[0] = (double)lam * sum_gap;
+    out[1] = sum_tv;
+    out[2] = sum_fid;
+    free(zv);
+    free(g);
+    return 0;
+}

@@ -391,3 +391,55 @@ def test_cone_matches_full_run(oracle_mod):
         assert np.array_equal(pc, p[(slice(None),) + c])
         assert np.array_equal(rc, r[(slice(None),) + c])
         assert zc == z[c]
+
+
+# --------------------------------------------------------------------------
+# duality gap in per-voxel form
+
+def test_gap_per_voxel_form_equals_definition(oracle_mod):
+    """In fp64 the oracle's per-voxel gap equals P(z) - d(p) from the definition."""
+    import phantoms
+    b = phantoms.make_b(0, dims=(9, 8, 7)).astype(np.float64) * 3.0
+    lam = 0.01
+    for k in (0, 1, 5, 40):
+        p0 = zeros_field(b.shape)
+        p, _ = oracle_mod.run(b, p0, p0, lam, 1, k, dtype=np.float64) if k else (p0, p0)
+        g_pv, tv, fid = oracle_mod.duality_gap(b, p, lam)
+        g_def = duality_gap(b, p, lam)  # matrix-built D, P(z) - d(p)
+        assert abs(g_pv - g_def) <= 1e-12 * max(1.0, abs(g_def)) + 1e-15
+        # the pieces: P(z) = fid + lam * tv
+        nz, ny, nx = b.shape
+        d = brute.difference_matrix(nx, ny, nz)
+        z = np.maximum(b.ravel() - lam * (d.T @ p.ravel()), 0.0)
+        dz = (d @ z).reshape(3, -1)
+        assert abs(tv - np.sqrt((dz ** 2).sum(axis=0)).sum()) < 1e-12 * max(tv, 1.0)
+        assert abs(fid - 0.5 * ((z - b.ravel()) ** 2).sum()) < 1e-12 * max(fid, 1.0)
+
+
+def test_gap_nonnegative_and_closing(oracle_mod):
+    import phantoms
+    b, p0, r0 = phantoms.make_inputs(0, (12, 10, 9))
+    lam = 0.01
+    prev = None
+    for k in (1, 10, 100, 400):
+        p, _ = oracle_mod.run(b, p0, r0, lam, 1, k)
+        g, tv, fid = oracle_mod.duality_gap(b, p, lam)
+        assert g >= -1e-9 * lam * tv  # |p| <= 1 + 5e-7 in fp32
+        if prev is not None:
+            assert g < prev
+        prev = g
+    g1 = oracle_mod.duality_gap(b, oracle_mod.run(b, p0, r0, lam, 1, 1)[0], lam)[0]
+    assert prev < 1e-3 * g1
+
+
+@pytest.mark.parametrize("row", read_golden("two_voxel.txt"))
+def test_gap_zero_at_two_voxel_optimum(oracle_mod, row):
+    """At the closed-form optimum (p = +1 on the only slot) the gap is 0."""
+    _, lam, b0, b1, z0, z1, pk = row[0], *map(float, row[1:])
+    b = np.array([b0, b1]).reshape(1, 1, 2)
+    p = zeros_field((1, 1, 2))
+    p[0, 0, 0, 0] = pk
+    g, tv, fid = oracle_mod.duality_gap(b, p, lam)
+    assert abs(g) < 1e-15
+    assert abs(tv - abs(z0 - z1)) < 1e-15
+    assert abs(fid - 0.5 * ((z0 - b0) ** 2 + (z1 - b1) ** 2)) < 1e-15
