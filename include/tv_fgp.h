@@ -25,8 +25,9 @@
  *     correctly rounded square root and division; every variant evaluates the
  *     same expressions in the same order, so all variants give the same bits.
  *   - Work is enqueued on `stream` (a hipStream_t; NULL is the null stream).
- *     Calls return as soon as the work is enqueued; they never synchronise
- *     the host.  Results are valid once the stream has completed.
+ *     Calls return as soon as the work is enqueued and do not synchronise
+ *     the host (the one exception, tv_fgp_solve, says so).  Results are
+ *     valid once the stream has completed.
  *   - Errors are negative status codes (below); nothing is enqueued when a
  *     call fails validation.  No call aborts, throws or prints.  NaN or Inf
  *     in the data is not checked; it propagates.
@@ -49,11 +50,11 @@ extern "C" {
 #define TV_ERR_DIMS      -2  /* a dimension < 1, or nx*ny*nz*4 bytes overflows        */
 #define TV_ERR_ALIAS     -3  /* a written buffer overlaps another buffer of the call  */
 #define TV_ERR_PARAM     -4  /* lambda <= 0 or not finite, 1/(12 lambda) not finite,
-                                m not finite, negative step counts                   */
-#define TV_ERR_WORKSPACE -5  /* the two-kernel variant was given no z workspace       */
+                                m not finite, negative step counts, NaN tolerance    */
+#define TV_ERR_WORKSPACE -5  /* a required workspace is missing or too small          */
 #define TV_ERR_VARIANT   -6  /* unknown variant                                      */
-#define TV_ERR_LAUNCH    -7  /* the HIP runtime reported an error at a launch         */
-#define TV_ERR_ALIGN     -8  /* a pointer is not 4-byte aligned                       */
+#define TV_ERR_LAUNCH    -7  /* the HIP runtime reported an error                     */
+#define TV_ERR_ALIGN     -8  /* a pointer is not aligned to its element size          */
 
 /* Kernel variants.  All give bit-identical results. */
 #define TV_FGP_FUSED      0  /* default: one fused pass; 64x8 x-y tiles march along
@@ -131,6 +132,59 @@ int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
  */
 int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
               int64_t nx, int64_t ny, int64_t nz, void *stream);
+
+/*
+ * Bytes of device workspace tv_fgp_duality_gap needs at these dimensions
+ * (at most 24 KiB); 0 for invalid dimensions.
+ */
+size_t tv_fgp_gap_workspace_bytes(int64_t nx, int64_t ny, int64_t nz);
+
+/*
+ * Duality gap of a dual field p for the problem the FGP iteration solves
+ * (minimise 1/2||z - b||^2 + lambda * sum_i |(Dz)(i)| over z >= 0; the page
+ * "TV solver: the FGP step on the GPU", section "What one step does", gives
+ * the step).  With z = max(b - lambda L(p), 0) and g = D z computed in fp32
+ * exactly as the step computes them, writes to the DEVICE buffer `out`:
+ *   out[0] = G = lambda * sum_i (|g(i)| - g(i).p(i))
+ *   out[1] = sum_i |g(i)|          (total variation of z)
+ *   out[2] = 1/2 sum_i (z(i) - b(i))^2
+ * G equals P(z) - d(p), the gap between the primal value
+ * P(z) = out[2] + lambda*out[1] and the dual value 1/2||b||^2 - 1/2||z||^2,
+ * because z (z - w) = 0 for z = max(w, 0) and <z, L p> = <D z, p> when the
+ * upper-face slots of p are zero; each term is >= 0 when |p(i)| <= 1, and
+ * G -> 0 as the iteration converges.  Per-voxel terms and sums are fp64; the
+ * sum order is fixed, so repeated calls give identical bits.
+ *   out        [out] device, 3 doubles, 8-byte aligned.
+ *   workspace  [scratch] device, tv_fgp_gap_workspace_bytes(...) bytes,
+ *              8-byte aligned; contents on return are unspecified.
+ * out and workspace must not overlap each other or b, p.  Enqueued on
+ * `stream`, no host synchronisation.
+ */
+int tv_fgp_duality_gap(const float *b, const float *const p[3], float lambda,
+                       int64_t nx, int64_t ny, int64_t nz, double *out,
+                       void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * The inner loop with a convergence check: outer iterations of n_inner steps
+ * (as tv_fgp_run, momentum restarted per outer iteration) until the duality
+ * gap of p satisfies G <= tol * P(z) (tv_fgp_duality_gap), or max_outer outer
+ * iterations have run.  The gap is computed before the first iteration and
+ * after each one.  THIS CALL SYNCHRONISES `stream`: the gap is copied to the
+ * host after each check.
+ *   gap_ws, gap_ws_bytes  workspace of tv_fgp_duality_gap
+ *   gap_dev     [out] device, 3 doubles (the last gap triple)
+ *   r_final     [out] host, may be NULL: 0 if the last r is in r_a, 1 if r_b
+ *   outer_done  [out] host, may be NULL: outer iterations run
+ *   gap_host    [out] host, 3 doubles: the last gap triple
+ * tol < 0 never stops early; tol NaN is TV_ERR_PARAM.  Other arguments and
+ * overlap rules as tv_fgp_run and tv_fgp_duality_gap.
+ */
+int tv_fgp_solve(const float *b, float *const p[3], float *const r_a[3],
+                 float *const r_b[3], float lambda, int max_outer, int n_inner,
+                 double tol, int64_t nx, int64_t ny, int64_t nz, int variant,
+                 float *z_ws, void *gap_ws, size_t gap_ws_bytes, double *gap_dev,
+                 void *stream, int *r_final, int *outer_done,
+                 double gap_host[3]);
 
 /*
  * Bytes of z workspace `variant` needs at these dimensions: nx*ny*nz*4 for

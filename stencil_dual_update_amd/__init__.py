@@ -3,11 +3,12 @@
 The computation runs in hand-written HIP kernels in ``libtvfgp.so`` behind a
 C ABI (``include/tv_fgp.h``); this package is its Python binding.  torch
 tensors provide device memory and streams.  See ``_lib`` for the entry
-points: ``tv_fgp_step``, ``tv_fgp_run``, ``tv_primal``.
+points: ``tv_fgp_step``, ``tv_fgp_run``, ``tv_primal``, ``tv_fgp_duality_gap``,
+``tv_fgp_solve``.
 """
 from ._lib import (  # noqa: F401
     EXPORTS, FUSED, LDS_MARCH, POINT, REG_MARCH, TWO_KERNEL, VARIANTS, LIB_PATH,
     TV_ERR_ALIAS, TV_ERR_ALIGN, TV_ERR_DIMS, TV_ERR_LAUNCH, TV_ERR_NULL,
     TV_ERR_PARAM, TV_ERR_VARIANT, TV_ERR_WORKSPACE, TV_OK, TvFgpError, lib,
-    momentum, status_string, tv_fgp_run, tv_fgp_step, tv_primal, variant_name,
-    workspace_bytes)
+    gap_workspace_bytes, momentum, status_string, tv_fgp_duality_gap, tv_fgp_run,
+    tv_fgp_solve, tv_fgp_step, tv_primal, variant_name, workspace_bytes)

@@ -31,6 +31,7 @@ VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
 
 # Names declared in include/tv_fgp.h, in declaration order.
 EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_primal",
+           "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
            "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_status_string",
            "tv_fgp_variant_name")
 
@@ -70,6 +71,15 @@ def _load():
                                ctypes.POINTER(ctypes.c_int)]
     lib.tv_primal.restype = ctypes.c_int
     lib.tv_primal.argtypes = [P, P3, P, F, I64, I64, I64, P]
+    lib.tv_fgp_gap_workspace_bytes.restype = ctypes.c_size_t
+    lib.tv_fgp_gap_workspace_bytes.argtypes = [I64, I64, I64]
+    lib.tv_fgp_duality_gap.restype = ctypes.c_int
+    lib.tv_fgp_duality_gap.argtypes = [P, P3, F, I64, I64, I64, P, P, ctypes.c_size_t, P]
+    lib.tv_fgp_solve.restype = ctypes.c_int
+    lib.tv_fgp_solve.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int, ctypes.c_double,
+                                 I64, I64, I64, ctypes.c_int, P, P, ctypes.c_size_t, P, P,
+                                 ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int),
+                                 ctypes.POINTER(ctypes.c_double)]
     lib.tv_fgp_workspace_bytes.restype = ctypes.c_size_t
     lib.tv_fgp_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
     lib.tv_fgp_momentum.restype = ctypes.c_float
@@ -113,6 +123,10 @@ def momentum(k):
 
 def workspace_bytes(variant, nx, ny, nz):
     return int(lib.tv_fgp_workspace_bytes(int(variant), nx, ny, nz))
+
+
+def gap_workspace_bytes(nx, ny, nz):
+    return int(lib.tv_fgp_gap_workspace_bytes(nx, ny, nz))
 
 
 # --------------------------------------------------------------------------
@@ -221,3 +235,55 @@ def tv_primal(b, p, z, lam, stream=None, dims=None):
     st = lib.tv_primal(_addr(b), _field(p, shape, "p"), _addr(z), float(lam),
                        nx, ny, nz, _stream(stream))
     _raise(st, "tv_primal")
+
+
+def _check_dev(t, what, dtype_name, numel):
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % what)
+    if str(t.dtype) != "torch." + dtype_name:
+        raise ValueError("%s must be %s" % (what, dtype_name))
+    if t.numel() < numel:
+        raise ValueError("%s needs at least %d elements" % (what, numel))
+
+
+def tv_fgp_duality_gap(b, p, lam, out, workspace, stream=None, dims=None):
+    """Gap triple (G, TV(z), 1/2||z-b||^2) of p into the float64 device tensor `out`."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_dev(out, "out", "float64", 3)
+    ws_bytes = gap_workspace_bytes(nx, ny, nz)
+    _check_dev(workspace, "workspace", "float64", ws_bytes // 8)
+    st = lib.tv_fgp_duality_gap(_addr(b), _field(p, shape, "p"), float(lam), nx, ny, nz,
+                                _addr(out), _addr(workspace),
+                                ws_bytes if not isinstance(workspace, int) else ws_bytes,
+                                _stream(stream))
+    _raise(st, "tv_fgp_duality_gap")
+
+
+def tv_fgp_solve(b, p, r_a, r_b, lam, max_outer, n_inner, tol, gap_ws, gap_dev,
+                 variant=FUSED, z_ws=None, stream=None, dims=None):
+    """Outer iterations until G <= tol * P(z) or max_outer; synchronises the stream.
+
+    Returns (outer_done, r_final, (G, TV(z), 1/2||z-b||^2)).
+    """
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_volume(z_ws, shape, "z_ws")
+    ws_bytes = gap_workspace_bytes(nx, ny, nz)
+    _check_dev(gap_ws, "gap_ws", "float64", ws_bytes // 8)
+    _check_dev(gap_dev, "gap_dev", "float64", 3)
+    where = ctypes.c_int(-1)
+    done = ctypes.c_int(-1)
+    host = (ctypes.c_double * 3)()
+    st = lib.tv_fgp_solve(_addr(b), _field(p, shape, "p"), _field(r_a, shape, "r_a"),
+                          _field(r_b, shape, "r_b"), float(lam), int(max_outer), int(n_inner),
+                          float(tol), nx, ny, nz, int(variant), _addr(z_ws), _addr(gap_ws),
+                          ws_bytes, _addr(gap_dev), _stream(stream), ctypes.byref(where),
+                          ctypes.byref(done), host)
+    _raise(st, "tv_fgp_solve")
+    return done.value, where.value, (host[0], host[1], host[2])

@@ -1,10 +1,10 @@
 // C-ABI layer of the FGP library: argument checks, the FISTA momentum
-// schedule, the r ping-pong of the inner loop, and dispatch to the kernel
-// launchers.  Everything here is host code; nothing allocates, synchronises
-// or touches device memory, and a call that fails validation enqueues
-// nothing.
+// schedule, the r ping-pong of the inner loop, the convergence-checked solve
+// loop, and dispatch to the kernel launchers.  Host code only.  A call that
+// fails validation enqueues nothing; only tv_fgp_solve synchronises.
 #include "tv_fgp.h"
 
+#include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
 #include <string.h>
@@ -27,26 +27,32 @@ size_t volume_bytes(int64_t nx, int64_t ny, int64_t nz) {
 
 struct Buf {
   const void *ptr;
+  size_t bytes;
+  size_t align;
   bool written;
 };
 
-// Every buffer must be non-null and 4-byte aligned, and a written buffer may
-// not overlap any other buffer.  All buffers span `bytes`.
-int check_buffers(const Buf *bufs, int count, size_t bytes) {
+// Every buffer must be non-null and aligned, and a written buffer may not
+// overlap any other buffer.
+int check_buffers(const Buf *bufs, int count) {
   for (int k = 0; k < count; ++k)
     if (bufs[k].ptr == nullptr) return TV_ERR_NULL;
   for (int k = 0; k < count; ++k)
-    if (((uintptr_t)bufs[k].ptr & (sizeof(float) - 1)) != 0) return TV_ERR_ALIGN;
+    if (((uintptr_t)bufs[k].ptr & (bufs[k].align - 1)) != 0) return TV_ERR_ALIGN;
   for (int k = 0; k < count; ++k) {
     const uintptr_t a = (uintptr_t)bufs[k].ptr;
-    if (a > UINTPTR_MAX - bytes) return TV_ERR_DIMS;
+    if (a > UINTPTR_MAX - bufs[k].bytes) return TV_ERR_DIMS;
     for (int l = k + 1; l < count; ++l) {
       if (!bufs[k].written && !bufs[l].written) continue;
       const uintptr_t c = (uintptr_t)bufs[l].ptr;
-      if (a < c + bytes && c < a + bytes) return TV_ERR_ALIAS;
+      if (a < c + bufs[l].bytes && c < a + bufs[k].bytes) return TV_ERR_ALIAS;
     }
   }
   return TV_OK;
+}
+
+Buf vol(const void *p, size_t bytes, bool written) {
+  return Buf{p, bytes, sizeof(float), written};
 }
 
 int check_lambda(float lambda, float *c_out) {
@@ -85,28 +91,36 @@ tvfgp::StepArgs make_step(const float *b, float *const p[3],
   return a;
 }
 
-// Shared checks of a step: variant, dimensions, lambda, m, buffers.
-int check_step(const float *b, float *const p[3], const float *const r_in[3],
-               float *const r_out[3], float lambda, float m, int64_t nx,
-               int64_t ny, int64_t nz, int variant, const float *z_ws,
-               float *c_out) {
-  if (!known_variant(variant)) return TV_ERR_VARIANT;
-  if (p == nullptr || r_in == nullptr || r_out == nullptr) return TV_ERR_NULL;
-  const size_t bytes = volume_bytes(nx, ny, nz);
-  if (bytes == 0) return TV_ERR_DIMS;
-  int st = check_lambda(lambda, c_out);
-  if (st != TV_OK) return st;
-  if (!isfinite(m)) return TV_ERR_PARAM;
-  const bool two = variant == tvfgp::kVariantTwoKernel;
-  if (two && z_ws == nullptr) return TV_ERR_WORKSPACE;
-  Buf bufs[11] = {{b, false},        {p[0], true},     {p[1], true},
-                  {p[2], true},      {r_in[0], false}, {r_in[1], false},
-                  {r_in[2], false},  {r_out[0], true}, {r_out[1], true},
-                  {r_out[2], true},  {z_ws, true}};
-  return check_buffers(bufs, two ? 11 : 10, bytes);
+int launch_status(int rc) { return rc == 0 ? TV_OK : TV_ERR_LAUNCH; }
+
+// Enqueue n_outer x n_inner steps; `where` (0: r_a holds r, 1: r_b) is
+// updated after every step, so the caller learns where the last r is.
+int enqueue_steps(const float *b, float *const p[3], float *const r_a[3],
+                  float *const r_b[3], float lambda, float c, int n_outer,
+                  int n_inner, int64_t nx, int64_t ny, int64_t nz, int variant,
+                  float *z_ws, void *stream, int *where) {
+  for (int o = 0; o < n_outer; ++o) {
+    double t = 1.0;
+    for (int k = 1; k <= n_inner; ++k) {
+      const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
+      const float m = (float)((t - 1.0) / t_next);
+      t = t_next;
+      float *const *in = *where ? r_b : r_a;
+      float *const *out = *where ? r_a : r_b;
+      const float *cin[3] = {in[0], in[1], in[2]};
+      const int rc = tvfgp::launch_step(make_step(b, p, cin, out, lambda, c, m,
+                                                  nx, ny, nz, variant, z_ws,
+                                                  stream));
+      if (rc != 0) return TV_ERR_LAUNCH;
+      *where ^= 1;
+    }
+  }
+  return TV_OK;
 }
 
-int launch_status(int rc) { return rc == 0 ? TV_OK : TV_ERR_LAUNCH; }
+size_t gap_ws_bytes(int64_t nx, int64_t ny, int64_t nz) {
+  return (size_t)tvfgp::gap_partial_count(nx, ny, nz) * 3 * sizeof(double);
+}
 
 }  // namespace
 
@@ -129,13 +143,26 @@ int tv_fgp_step_ex(const float *b, float *const p[3],
                    const float *const r_in[3], float *const r_out[3],
                    float lambda, float m, int64_t nx, int64_t ny, int64_t nz,
                    int variant, float *z_ws, void *stream) {
+  if (!known_variant(variant)) return TV_ERR_VARIANT;
+  if (p == nullptr || r_in == nullptr || r_out == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
   float c = 0.0f;
-  const int st =
-      check_step(b, p, r_in, r_out, lambda, m, nx, ny, nz, variant, z_ws, &c);
+  int st = check_lambda(lambda, &c);
   if (st != TV_OK) return st;
-  return launch_status(tvfgp::launch_step(
-      make_step(b, p, r_in, r_out, lambda, c, m, nx, ny, nz, variant, z_ws,
-                stream)));
+  if (!isfinite(m)) return TV_ERR_PARAM;
+  const bool two = variant == tvfgp::kVariantTwoKernel;
+  if (two && z_ws == nullptr) return TV_ERR_WORKSPACE;
+  const Buf bufs[11] = {vol(b, bytes, false),        vol(p[0], bytes, true),
+                        vol(p[1], bytes, true),      vol(p[2], bytes, true),
+                        vol(r_in[0], bytes, false),  vol(r_in[1], bytes, false),
+                        vol(r_in[2], bytes, false),  vol(r_out[0], bytes, true),
+                        vol(r_out[1], bytes, true),  vol(r_out[2], bytes, true),
+                        vol(z_ws, bytes, true)};
+  st = check_buffers(bufs, two ? 11 : 10);
+  if (st != TV_OK) return st;
+  return launch_status(tvfgp::launch_step(make_step(
+      b, p, r_in, r_out, lambda, c, m, nx, ny, nz, variant, z_ws, stream)));
 }
 
 int tv_fgp_step(const float *b, float *const p[3], const float *const r_in[3],
@@ -145,51 +172,44 @@ int tv_fgp_step(const float *b, float *const p[3], const float *const r_in[3],
                         tvfgp::kVariantFused, nullptr, stream);
 }
 
+// Checks shared by tv_fgp_run and tv_fgp_solve for the step buffers.
+static int check_run(const float *b, float *const p[3], float *const r_a[3],
+                     float *const r_b[3], float lambda, int64_t nx, int64_t ny,
+                     int64_t nz, int variant, float *z_ws, float *c_out,
+                     size_t *bytes_out) {
+  if (!known_variant(variant)) return TV_ERR_VARIANT;
+  if (p == nullptr || r_a == nullptr || r_b == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  int st = check_lambda(lambda, c_out);
+  if (st != TV_OK) return st;
+  const bool two = variant == tvfgp::kVariantTwoKernel;
+  if (two && z_ws == nullptr) return TV_ERR_WORKSPACE;
+  const Buf bufs[11] = {vol(b, bytes, false),     vol(p[0], bytes, true),
+                        vol(p[1], bytes, true),   vol(p[2], bytes, true),
+                        vol(r_a[0], bytes, true), vol(r_a[1], bytes, true),
+                        vol(r_a[2], bytes, true), vol(r_b[0], bytes, true),
+                        vol(r_b[1], bytes, true), vol(r_b[2], bytes, true),
+                        vol(z_ws, bytes, true)};
+  *bytes_out = bytes;
+  return check_buffers(bufs, two ? 11 : 10);
+}
+
 int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
                float *const r_b[3], float lambda, int n_outer, int n_inner,
                int64_t nx, int64_t ny, int64_t nz, int variant, float *z_ws,
                void *stream, int *r_final) {
   if (r_final) *r_final = 0;
-  if (!known_variant(variant)) return TV_ERR_VARIANT;
-  if (p == nullptr || r_a == nullptr || r_b == nullptr) return TV_ERR_NULL;
-  const size_t bytes = volume_bytes(nx, ny, nz);
-  if (bytes == 0) return TV_ERR_DIMS;
-  if (n_outer < 0 || n_inner < 0) return TV_ERR_PARAM;
   float c = 0.0f;
-  int st = check_lambda(lambda, &c);
+  size_t bytes = 0;
+  int st = check_run(b, p, r_a, r_b, lambda, nx, ny, nz, variant, z_ws, &c, &bytes);
   if (st != TV_OK) return st;
-  const bool two = variant == tvfgp::kVariantTwoKernel;
-  if (two && z_ws == nullptr) return TV_ERR_WORKSPACE;
-  Buf bufs[11] = {{b, false},     {p[0], true},   {p[1], true},  {p[2], true},
-                  {r_a[0], true}, {r_a[1], true}, {r_a[2], true}, {r_b[0], true},
-                  {r_b[1], true}, {r_b[2], true}, {z_ws, true}};
-  st = check_buffers(bufs, two ? 11 : 10, bytes);
-  if (st != TV_OK) return st;
-
-  const float *cur_in[3] = {r_a[0], r_a[1], r_a[2]};
-  float *cur_out[3] = {r_b[0], r_b[1], r_b[2]};
+  if (n_outer < 0 || n_inner < 0) return TV_ERR_PARAM;
   int where = 0;
-  for (int o = 0; o < n_outer; ++o) {
-    double t = 1.0;
-    for (int k = 1; k <= n_inner; ++k) {
-      const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
-      const float m = (float)((t - 1.0) / t_next);
-      t = t_next;
-      const int rc = tvfgp::launch_step(make_step(b, p, cur_in, cur_out, lambda,
-                                                  c, m, nx, ny, nz, variant,
-                                                  z_ws, stream));
-      if (rc != 0) return TV_ERR_LAUNCH;
-      where ^= 1;
-      float *const *next_in = where ? r_b : r_a;
-      float *const *next_out = where ? r_a : r_b;
-      for (int a = 0; a < 3; ++a) {
-        cur_in[a] = next_in[a];
-        cur_out[a] = next_out[a];
-      }
-      if (r_final) *r_final = where;
-    }
-  }
-  return TV_OK;
+  st = enqueue_steps(b, p, r_a, r_b, lambda, c, n_outer, n_inner, nx, ny, nz,
+                     variant, z_ws, stream, &where);
+  if (r_final) *r_final = where;
+  return st;
 }
 
 int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
@@ -200,9 +220,10 @@ int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
   float c = 0.0f;
   int st = check_lambda(lambda, &c);
   if (st != TV_OK) return st;
-  Buf bufs[5] = {{b, false}, {p[0], false}, {p[1], false}, {p[2], false},
-                 {z, true}};
-  st = check_buffers(bufs, 5, bytes);
+  const Buf bufs[5] = {vol(b, bytes, false), vol(p[0], bytes, false),
+                       vol(p[1], bytes, false), vol(p[2], bytes, false),
+                       vol(z, bytes, true)};
+  st = check_buffers(bufs, 5);
   if (st != TV_OK) return st;
   tvfgp::PrimalArgs a;
   a.b = b;
@@ -217,6 +238,111 @@ int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
   return launch_status(tvfgp::launch_primal(a));
 }
 
+size_t tv_fgp_gap_workspace_bytes(int64_t nx, int64_t ny, int64_t nz) {
+  if (volume_bytes(nx, ny, nz) == 0) return 0;
+  return gap_ws_bytes(nx, ny, nz);
+}
+
+// Checks of the gap buffers; bytes of one volume in *bytes_out.
+static int check_gap(const float *b, const float *const p[3], float lambda,
+                     int64_t nx, int64_t ny, int64_t nz, double *out,
+                     void *workspace, size_t workspace_bytes,
+                     const Buf *extra, int n_extra) {
+  if (p == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  const size_t ws = gap_ws_bytes(nx, ny, nz);
+  if (workspace == nullptr || out == nullptr) return TV_ERR_NULL;
+  if (workspace_bytes < ws) return TV_ERR_WORKSPACE;
+  Buf bufs[16];
+  int n = 0;
+  bufs[n++] = vol(b, bytes, false);
+  for (int k = 0; k < 3; ++k) bufs[n++] = vol(p[k], bytes, false);
+  bufs[n++] = Buf{out, 3 * sizeof(double), sizeof(double), true};
+  bufs[n++] = Buf{workspace, ws, sizeof(double), true};
+  for (int k = 0; k < n_extra; ++k) bufs[n++] = extra[k];
+  return check_buffers(bufs, n);
+}
+
+int tv_fgp_duality_gap(const float *b, const float *const p[3], float lambda,
+                       int64_t nx, int64_t ny, int64_t nz, double *out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
+  const int st = check_gap(b, p, lambda, nx, ny, nz, out, workspace,
+                           workspace_bytes, nullptr, 0);
+  if (st != TV_OK) return st;
+  tvfgp::GapArgs a;
+  a.b = b;
+  for (int k = 0; k < 3; ++k) a.p[k] = p[k];
+  a.lam = lambda;
+  a.nx = nx;
+  a.ny = ny;
+  a.nz = nz;
+  a.out = out;
+  a.partial = (double *)workspace;
+  a.stream = stream;
+  return launch_status(tvfgp::launch_duality_gap(a));
+}
+
+int tv_fgp_solve(const float *b, float *const p[3], float *const r_a[3],
+                 float *const r_b[3], float lambda, int max_outer, int n_inner,
+                 double tol, int64_t nx, int64_t ny, int64_t nz, int variant,
+                 float *z_ws, void *gap_ws, size_t gap_ws_bytes_given,
+                 double *gap_dev, void *stream, int *r_final, int *outer_done,
+                 double gap_host[3]) {
+  if (r_final) *r_final = 0;
+  if (outer_done) *outer_done = 0;
+  float c = 0.0f;
+  size_t bytes = 0;
+  int st = check_run(b, p, r_a, r_b, lambda, nx, ny, nz, variant, z_ws, &c, &bytes);
+  if (st != TV_OK) return st;
+  if (max_outer < 0 || n_inner < 0 || isnan(tol)) return TV_ERR_PARAM;
+  if (gap_host == nullptr) return TV_ERR_NULL;
+  // the gap buffers may not overlap anything the steps write
+  Buf extra[7];
+  int n_extra = 0;
+  for (int k = 0; k < 3; ++k) {
+    extra[n_extra++] = vol(r_a[k], bytes, true);
+    extra[n_extra++] = vol(r_b[k], bytes, true);
+  }
+  if (variant == tvfgp::kVariantTwoKernel) extra[n_extra++] = vol(z_ws, bytes, true);
+  st = check_gap(b, p, lambda, nx, ny, nz, gap_dev, gap_ws, gap_ws_bytes_given,
+                 extra, n_extra);
+  if (st != TV_OK) return st;
+
+  tvfgp::GapArgs g;
+  g.b = b;
+  for (int k = 0; k < 3; ++k) g.p[k] = p[k];
+  g.lam = lambda;
+  g.nx = nx;
+  g.ny = ny;
+  g.nz = nz;
+  g.out = gap_dev;
+  g.partial = (double *)gap_ws;
+  g.stream = stream;
+  hipStream_t s = (hipStream_t)stream;
+  int where = 0;
+  int done = 0;
+  for (;;) {
+    if (tvfgp::launch_duality_gap(g) != 0) return TV_ERR_LAUNCH;
+    if (hipMemcpyAsync(gap_host, gap_dev, 3 * sizeof(double),
+                       hipMemcpyDeviceToHost, s) != hipSuccess)
+      return TV_ERR_LAUNCH;
+    if (hipStreamSynchronize(s) != hipSuccess) return TV_ERR_LAUNCH;
+    const double primal = gap_host[2] + (double)lambda * gap_host[1];
+    if (done >= max_outer || gap_host[0] <= tol * primal) break;
+    st = enqueue_steps(b, p, r_a, r_b, lambda, c, 1, n_inner, nx, ny, nz,
+                       variant, z_ws, stream, &where);
+    if (st != TV_OK) return st;
+    ++done;
+    if (r_final) *r_final = where;
+    if (outer_done) *outer_done = done;
+  }
+  return TV_OK;
+}
+
 size_t tv_fgp_workspace_bytes(int variant, int64_t nx, int64_t ny, int64_t nz) {
   if (!known_variant(variant)) return 0;
   if (variant != tvfgp::kVariantTwoKernel) return 0;
@@ -229,11 +355,11 @@ const char *tv_fgp_status_string(int status) {
     case TV_ERR_NULL: return "a required pointer is NULL";
     case TV_ERR_DIMS: return "invalid dimensions (< 1 or size overflow)";
     case TV_ERR_ALIAS: return "a written buffer overlaps another buffer";
-    case TV_ERR_PARAM: return "invalid parameter (lambda, m or step count)";
-    case TV_ERR_WORKSPACE: return "the two-kernel variant needs a z workspace";
+    case TV_ERR_PARAM: return "invalid parameter (lambda, m, tolerance or step count)";
+    case TV_ERR_WORKSPACE: return "missing or too small workspace";
     case TV_ERR_VARIANT: return "unknown variant";
-    case TV_ERR_LAUNCH: return "the HIP runtime reported a launch error";
-    case TV_ERR_ALIGN: return "a pointer is not 4-byte aligned";
+    case TV_ERR_LAUNCH: return "the HIP runtime reported an error";
+    case TV_ERR_ALIGN: return "a pointer is not aligned to its element size";
     default: return "unknown status";
   }
 }

@@ -46,11 +46,25 @@ struct PrimalArgs {
   void *stream;
 };
 
+struct GapArgs {
+  const float *b;
+  const float *p[3];
+  float lam;
+  int64_t nx, ny, nz;
+  double *out;      // 3 doubles, device
+  double *partial;  // 3 * gap_partial_count(...) doubles, device
+  void *stream;
+};
+
 // Enqueue one step / one read-out.  Return 0, or kLaunchFailed when the HIP
 // runtime reports an error after a launch.
 int launch_step(const StepArgs &a);
 int launch_primal(const PrimalArgs &a);
 int launch_lds_march(const StepArgs &a);
 int launch_fused_zx(const StepArgs &a);
+// Duality gap of p (two kernels: partial sums, then their fixed-order sum).
+int launch_duality_gap(const GapArgs &a);
+// Partial triples the gap reduction writes for these dimensions.
+int gap_partial_count(int64_t nx, int64_t ny, int64_t nz);
 
 }  // namespace tvfgp

@@ -9,7 +9,7 @@
 // checked here (barriers are no-ops), only addresses.
 //
 // usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
-//   variant: fused | fused_nostream | reg_march | point | two_kernel | lds_march | primal
+//   variant: fused | fused_nostream | reg_march | point | two_kernel | lds_march | primal | gap
 //   wide: 1 instantiates the 64-bit offset / index path regardless of size
 #include <stdio.h>
 #include <stdlib.h>
@@ -19,6 +19,7 @@
 #include "tv_fgp_ablation_kernels.hpp"
 #include "tv_fgp_device.hpp"
 #include "tv_fgp_fused_kernel.hpp"
+#include "tv_fgp_gap_kernel.hpp"
 #include "tv_fgp_lds_kernel.hpp"
 
 thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
@@ -118,6 +119,15 @@ void run_ablation(const char *variant, const Bufs &v, int64_t nx, int64_t ny, in
         dual_kernel<I>(v.z, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2], v.ro[0],
                        v.ro[1], v.ro[2], 8.3f, 0.5f, g);
       });
+  } else if (!strcmp(variant, "gap")) {
+    const Geometry<I> g = make_geometry<I>(nx, ny, nz, kGapPlanes);
+    const int count = grid ? (int)grid : gap_grid(nx, ny, nz);
+    double *partial = (double *)guarded((size_t)count * 3 * sizeof(double), true, 99);
+    double *out = (double *)guarded(3 * sizeof(double), true, 98);
+    run_grid((unsigned)count, kBlock, [&] {
+      gap_partial_kernel<I>(v.b, v.p[0], v.p[1], v.p[2], 0.01f, g, partial);
+    });
+    run_grid(1, kGapFinalBlock, [&] { gap_final_kernel(partial, count, 0.01, out); });
   } else if (!strcmp(variant, "lds_march")) {
     const Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
     run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {

@@ -203,3 +203,65 @@ def test_python_binding_raises():
     assert tvf.tv_fgp_run(addr(0), [addr(1), addr(2), addr(3)], [addr(4), addr(5), addr(6)],
                           [addr(7), addr(8), addr(9)], 0.01, 0, 10, stream=0,
                           dims=(NX, NY, NZ)) == 0
+
+
+def test_gap_workspace_bytes():
+    assert 0 < tvf.gap_workspace_bytes(NX, NY, NZ) <= 24 * 1024
+    assert tvf.gap_workspace_bytes(4096, 4096, 4096) == 3 * 8 * 1024
+    assert tvf.gap_workspace_bytes(0, 1, 1) == 0
+
+
+def gap(b=0, p=(1, 2, 3), lam=0.01, out=20, ws=21, ws_bytes=None, dims=(NX, NY, NZ)):
+    wsb = tvf.gap_workspace_bytes(*dims) if ws_bytes is None else ws_bytes
+    return L.tv_fgp_duality_gap(None if b is None else addr(b), field(*p), lam, *dims,
+                                None if out is None else addr(out),
+                                None if ws is None else addr(ws), wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=None), tvf.TV_ERR_NULL),
+    (dict(out=None), tvf.TV_ERR_NULL),
+    (dict(ws=None), tvf.TV_ERR_NULL),
+    (dict(p=(1, None, 3)), tvf.TV_ERR_NULL),
+    (dict(ws_bytes=8), tvf.TV_ERR_WORKSPACE),
+    (dict(lam=0.0), tvf.TV_ERR_PARAM),
+    (dict(dims=(NX, 0, NZ)), tvf.TV_ERR_DIMS),
+    (dict(out=1), tvf.TV_ERR_ALIAS),   # out inside p[0]
+    (dict(ws=0), tvf.TV_ERR_ALIAS),    # workspace inside b
+    (dict(out=21), tvf.TV_ERR_ALIAS),  # out inside the workspace
+])
+def test_gap_rejects(kw, code):
+    assert gap(**kw) == code
+
+
+def test_gap_misaligned_out():
+    assert L.tv_fgp_duality_gap(addr(0), field(1, 2, 3), 0.01, NX, NY, NZ, addr(20) + 4,
+                                addr(21), tvf.gap_workspace_bytes(NX, NY, NZ), None) \
+        == tvf.TV_ERR_ALIGN
+
+
+def solve(max_outer=3, n_inner=5, tol=1e-3, ra=(4, 5, 6), rb=(7, 8, 9), gws=21, gdev=20,
+          lam=0.01, host=True):
+    where, done = ctypes.c_int(-5), ctypes.c_int(-5)
+    gh = (ctypes.c_double * 3)()
+    st = L.tv_fgp_solve(addr(0), field(1, 2, 3), field(*ra), field(*rb), lam, max_outer, n_inner,
+                        tol, NX, NY, NZ, 0, None, addr(gws),
+                        tvf.gap_workspace_bytes(NX, NY, NZ), addr(gdev), None,
+                        ctypes.byref(where), ctypes.byref(done), gh if host else None)
+    return st, where.value, done.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(max_outer=-1), tvf.TV_ERR_PARAM),
+    (dict(n_inner=-1), tvf.TV_ERR_PARAM),
+    (dict(tol=float("nan")), tvf.TV_ERR_PARAM),
+    (dict(lam=-1.0), tvf.TV_ERR_PARAM),
+    (dict(host=False), tvf.TV_ERR_NULL),
+    (dict(gdev=7), tvf.TV_ERR_ALIAS),      # gap output inside r_b[0]
+    (dict(gws=4), tvf.TV_ERR_ALIAS),       # gap workspace inside r_a[0]
+    (dict(rb=(7, 8, 5)), tvf.TV_ERR_ALIAS),
+])
+def test_solve_rejects(kw, code):
+    st, where, done = solve(**kw)
+    assert st == code
+    assert where == 0 and done == 0
