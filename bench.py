@@ -16,6 +16,8 @@ Besides the headline ms/step it reports:
                 committed under profiles/ (null when the kernel sources have
                 changed since those counters were taken); `bench.py --traffic`
                 builds that record from the two counter runs
+  gap_kernel    time of one duality-gap evaluation of the final p (reads b and
+                p: 16 B per voxel) and the gap triple itself
   copy          bandwidth of a plain device copy of 2 x 1 GiB on the same box
   cpu_baseline  the CPU oracle (fp32, OpenMP) timed on the host cores on a
                 bounded sample: the first 10 outer iterations (100 steps) of
@@ -203,6 +205,29 @@ def main():
     achieved = step_bytes / (launch_avg_ms * 1e-3) / 1e9
     region_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
+    # duality-gap reduction (reads b and p: 16 B per voxel)
+    gap_ws = torch.empty(tvf.gap_workspace_bytes(nx, ny, nz) // 8, dtype=torch.float64,
+                         device=dev)
+    gap_out = torch.empty(3, dtype=torch.float64, device=dev)
+    with torch.cuda.stream(stream):
+        for _ in range(3):
+            tvf.tv_fgp_duality_gap(b, p, lam, gap_out, gap_ws, stream=stream)
+        g0 = torch.cuda.Event(enable_timing=True)
+        g1 = torch.cuda.Event(enable_timing=True)
+        g0.record(stream)
+        gap_reps = 20
+        for _ in range(gap_reps):
+            tvf.tv_fgp_duality_gap(b, p, lam, gap_out, gap_ws, stream=stream)
+        g1.record(stream)
+        torch.cuda.synchronize()
+    gap_ms = g0.elapsed_time(g1) / gap_reps
+    gap_vals = gap_out.cpu().tolist()
+    gap = {"ms": round(gap_ms, 5), "algorithmic_bytes": 16 * nvox,
+           "gbps": round(16 * nvox / (gap_ms * 1e-3) / 1e9, 1),
+           "frac_of_hbm_peak": round(16 * nvox / (gap_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+           "gap": gap_vals[0], "tv": gap_vals[1], "fidelity": gap_vals[2]}
+    del gap_ws, gap_out
+
     copy = None
     if not args.no_copy:
         src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
@@ -268,6 +293,7 @@ def main():
                      "launch_ms_avg": round(launch_avg_ms, 5),
                      "launch_ms_min": round(float(np.min(launch_ms)), 5),
                      "launch_ms_max": round(float(np.max(launch_ms)), 5)},
+        "gap_kernel": gap,
         "copy": copy,
         "pct_of_copy": (round(100.0 * region_gbs / copy["gbps"], 1) if copy else None),
         "cpu_baseline": cpu,
