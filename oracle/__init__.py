@@ -56,6 +56,17 @@ def _load():
         f = getattr(lib, "tv_oracle_duality_gap_" + suf)
         f.restype = ctypes.c_int
         f.argtypes = [P] * 4 + [real, I64, I64, I64, P]
+    lib.tv_oracle_f16_to_f32.restype = ctypes.c_float
+    lib.tv_oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.tv_oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.tv_oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.tv_oracle_f32_to_f16_array.restype = None
+    lib.tv_oracle_f32_to_f16_array.argtypes = [P, P, I64]
+    lib.tv_oracle_f16_to_f32_array.restype = None
+    lib.tv_oracle_f16_to_f32_array.argtypes = [P, P, I64]
+    lib.tv_oracle_run_h.restype = ctypes.c_int
+    lib.tv_oracle_run_h.argtypes = [P] * 7 + [ctypes.c_float, ctypes.c_int, ctypes.c_int,
+                                               I64, I64, I64]
     _lib = lib
     return lib
 
@@ -183,6 +194,40 @@ def run(b, p0, r0, lam, n_outer, n_inner, dtype=None):
         real(lam), int(n_outer), int(n_inner), *_dims(b))
     if rc != 0:
         raise MemoryError("oracle run could not allocate scratch")
+    return p, r
+
+
+def f32_to_f16_bits(v):
+    """binary16 bit patterns of float32 values (nearest, ties to even), same shape."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    out = np.empty(v.shape, dtype=np.uint16)
+    _load().tv_oracle_f32_to_f16_array(_ptr(v), _ptr(out), v.size)
+    return out
+
+
+def f16_bits_to_f32(h):
+    """float32 values of binary16 bit patterns (exact), same shape."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, dtype=np.float32)
+    _load().tv_oracle_f16_to_f32_array(_ptr(h), _ptr(out), h.size)
+    return out
+
+
+def run_half(b, p0_bits, r0_bits, lam, n_outer, n_inner):
+    """FGP with p and r stored as binary16 (uint16 bit patterns, (3, nz, ny, nx)).
+
+    b is float32; arithmetic is float32; p and r are rounded to binary16 after
+    every step.  Returns (p_bits, r_bits) copies.
+    """
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    p = np.array(p0_bits, dtype=np.uint16, copy=True, order="C")
+    r = np.array(r0_bits, dtype=np.uint16, copy=True, order="C")
+    assert p.shape == (3,) + b.shape and r.shape == p.shape
+    rc = _load().tv_oracle_run_h(
+        _ptr(b), _ptr(p[0]), _ptr(p[1]), _ptr(p[2]), _ptr(r[0]), _ptr(r[1]), _ptr(r[2]),
+        float(lam), int(n_outer), int(n_inner), *_dims(b))
+    if rc != 0:
+        raise MemoryError("oracle half run could not allocate scratch")
     return p, r
 
 

@@ -67,6 +67,92 @@ int tv_oracle_get_threads(void)
 #endif
 }
 
+/*
+ * IEEE-754 binary16 storage for the half-precision dual.  Conversions written
+ * from the format's definition: binary16 has 1 sign bit, 5 exponent bits
+ * (bias 15) and 10 fraction bits; its subnormals are k * 2^-24.
+ */
+
+/* binary16 -> binary32: exact. */
+float tv_oracle_f16_to_f32(uint16_t h)
+{
+    const uint32_t sign = (uint32_t)(h & 0x8000u) << 16;
+    const uint32_t e = (h >> 10) & 0x1Fu;
+    const uint32_t f = h & 0x3FFu;
+    uint32_t bits;
+    float out;
+    if (e == 0) {
+        /* zero or subnormal: f * 2^-24, exact in binary32 */
+        out = (float)f * (1.0f / 16777216.0f);
+        return (h & 0x8000u) ? -out : out;
+    }
+    if (e == 31)
+        bits = sign | 0x7F800000u | (f << 13);
+    else
+        bits = sign | ((e - 15u + 127u) << 23) | (f << 13);
+    memcpy(&out, &bits, sizeof out);
+    return out;
+}
+
+/*
+ * binary32 -> binary16, round to nearest, ties to even.  |v| is written as
+ * m * 2^(E-150) with a 24-bit m; the binary16 quantum at that magnitude is
+ * 2^(max(E-127, -14) - 10); the quotient is rounded half-to-even, and a carry
+ * into the next binade or past the largest finite value (to infinity) falls
+ * out of adding it to the exponent field.  NaN gives the quiet NaN 0x7E00
+ * with the input's sign.
+ */
+uint16_t tv_oracle_f32_to_f16(float v)
+{
+    uint32_t x;
+    memcpy(&x, &v, sizeof x);
+    const uint16_t sign = (uint16_t)((x >> 16) & 0x8000u);
+    const int e = (int)((x >> 23) & 0xFFu);
+    uint32_t m = x & 0x7FFFFFu;
+    if (e == 255)
+        return (uint16_t)(sign | (m ? 0x7E00u : 0x7C00u));
+    if (e != 0)
+        m |= 0x800000u;
+    const int e_unb = (e == 0) ? -126 : e - 127;
+    const int q_exp = (e_unb > -14 ? e_unb : -14) - 10;  /* quantum 2^q_exp */
+    const int value_exp = (e == 0) ? -149 : e - 150;     /* |v| = m * 2^value_exp */
+    const int sh = q_exp - value_exp;                      /* >= 13 */
+    uint32_t k;
+    if (sh >= 32) {
+        k = 0;
+    } else {
+        k = m >> sh;
+        const uint32_t rem = m & ((1u << sh) - 1u);
+        const uint32_t half = 1u << (sh - 1);
+        if (rem > half || (rem == half && (k & 1u)))
+            k += 1;
+    }
+    uint32_t bits;
+    if (e_unb < -14) {
+        bits = k;                               /* subnormal; k == 1024 is 2^-14 */
+    } else {
+        const uint32_t eb = (uint32_t)(e_unb + 15);
+        if (eb >= 31)
+            return (uint16_t)(sign | 0x7C00u);
+        bits = (eb << 10) + (k - 1024u);        /* k == 2048 carries into eb + 1 */
+    }
+    if (bits >= 0x7C00u)
+        bits = 0x7C00u;
+    return (uint16_t)(sign | bits);
+}
+
+void tv_oracle_f32_to_f16_array(const float *in, uint16_t *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = tv_oracle_f32_to_f16(in[i]);
+}
+
+void tv_oracle_f16_to_f32_array(const uint16_t *in, float *out, int64_t n)
+{
+    for (int64_t i = 0; i < n; ++i)
+        out[i] = tv_oracle_f16_to_f32(in[i]);
+}
+
 #define REAL float
 #define SQRT sqrtf
 #define FN(name) name##_f32
@@ -82,3 +168,48 @@ int tv_oracle_get_threads(void)
 #undef REAL
 #undef SQRT
 #undef FN
+
+/*
+ * FGP with the dual p and its momentum copy r stored in binary16, b in
+ * binary32, arithmetic in binary32: every step widens p and r exactly, runs
+ * the binary32 step (same code as tv_oracle_run_f32), and rounds the new p
+ * and r to binary16 (nearest, ties to even).
+ */
+int tv_oracle_run_h(const float *b, uint16_t *p0, uint16_t *p1, uint16_t *p2,
+                    uint16_t *r0, uint16_t *r1, uint16_t *r2, float lam,
+                    int n_outer, int n_inner, int64_t nx, int64_t ny, int64_t nz)
+{
+    const int64_t n = nx * ny * nz;
+    uint16_t *ph[3] = {p0, p1, p2};
+    uint16_t *rh[3] = {r0, r1, r2};
+    float *buf = (float *)malloc((size_t)n * 9 * sizeof(float));
+    if (!buf)
+        return -1;
+    float *pf[3] = {buf, buf + n, buf + 2 * n};
+    float *rf[3] = {buf + 3 * n, buf + 4 * n, buf + 5 * n};
+    float *rn[3] = {buf + 6 * n, buf + 7 * n, buf + 8 * n};
+    for (int o = 0; o < n_outer; ++o) {
+        for (int k = 1; k <= n_inner; ++k) {
+            const float m = (float)tv_oracle_momentum(k);
+            for (int a = 0; a < 3; ++a) {
+                for (int64_t i = 0; i < n; ++i) {
+                    pf[a][i] = tv_oracle_f16_to_f32(ph[a][i]);
+                    rf[a][i] = tv_oracle_f16_to_f32(rh[a][i]);
+                }
+            }
+            if (tv_oracle_step_f32(b, pf[0], pf[1], pf[2], rf[0], rf[1], rf[2],
+                                   rn[0], rn[1], rn[2], lam, m, nx, ny, nz) != 0) {
+                free(buf);
+                return -1;
+            }
+            for (int a = 0; a < 3; ++a) {
+                for (int64_t i = 0; i < n; ++i) {
+                    ph[a][i] = tv_oracle_f32_to_f16(pf[a][i]);
+                    rh[a][i] = tv_oracle_f32_to_f16(rn[a][i]);
+                }
+            }
+        }
+    }
+    free(buf);
+    return 0;
+}
