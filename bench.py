@@ -21,7 +21,12 @@ Besides the headline ms/step it reports:
   copy          bandwidth of a plain device copy of 2 x 1 GiB on the same box
   cpu_baseline  the CPU oracle (fp32, OpenMP) timed on the host cores on a
                 bounded sample: the first 10 outer iterations (100 steps) of
-                the same workload at full size
+                the same workload at full size (with --storage half: the first
+                outer iteration, 10 steps, of the oracle's half mode)
+
+--storage half runs the same step with p and r stored as binary16 (fp32
+arithmetic; 28 B per voxel: read b, r (3), p (3) at 4 + 6 + 6 B, write p (3),
+r (3) at 6 + 6 B); its CPU baseline is the oracle's half mode.
 """
 import argparse
 import hashlib
@@ -34,6 +39,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "reg_march": 52,
                    "two_kernel": 72}
+BYTES_PER_VOXEL_HALF = 28
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_512.json")
 METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
 
@@ -117,6 +123,8 @@ def parse():
                     choices=sorted(BYTES_PER_VOXEL))
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg")
+    ap.add_argument("--storage", default="f32", choices=["f32", "half"],
+                    help="storage of the dual p and r (half: binary16, fused kernel only)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy probe")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: build the traffic record under profiles/ from "
@@ -148,6 +156,10 @@ def main():
     lam = w["lam"]
     n_inner = w["n_inner"]
     variant = tvf.VARIANTS[args.variant]
+    half = args.storage == "half"
+    if half and args.variant != "fused":
+        print("--storage half runs the fused kernel only", file=sys.stderr)
+        return 2
     nvox = nx * ny * nz
 
     t0 = time.time()
@@ -155,11 +167,26 @@ def main():
     gen_s = time.time() - t0
     b = torch.from_numpy(b_host).to(dev)
     p = torch.from_numpy(p0_host).to(dev)
+    if half:
+        p = p.to(torch.float16)  # round to nearest even, as the oracle's half mode
     ra = p.clone()
     rb = torch.empty_like(ra)
     ws = torch.empty_like(b) if variant == tvf.TWO_KERNEL else None
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
+
+    def run(r_cur, r_nxt, n_outer, ni):
+        if half:
+            return tvf.tv_fgp_run_h(b, p, r_cur, r_nxt, lam, n_outer, ni, stream=stream)
+        return tvf.tv_fgp_run(b, p, r_cur, r_nxt, lam, n_outer, ni, variant=variant, z_ws=ws,
+                              stream=stream)
+
+    def step(r_cur, r_nxt, m):
+        if half:
+            tvf.tv_fgp_step_h(b, p, r_cur, r_nxt, lam, m, stream=stream)
+        else:
+            tvf.tv_fgp_step(b, p, r_cur, r_nxt, lam, m, variant=variant, z_ws=ws,
+                            stream=stream)
 
     def run_steps(k, r_cur, r_nxt):
         """k steps in outer iterations of n_inner; returns (r_cur, r_nxt) after."""
@@ -167,9 +194,7 @@ def main():
         for n_outer, ni in ((full, n_inner), (1 if rest else 0, rest)):
             if n_outer * ni == 0:
                 continue
-            where = tvf.tv_fgp_run(b, p, r_cur, r_nxt, lam, n_outer, ni,
-                                   variant=variant, z_ws=ws, stream=stream)
-            if where:
+            if run(r_cur, r_nxt, n_outer, ni):
                 r_cur, r_nxt = r_nxt, r_cur
         return r_cur, r_nxt
 
@@ -192,20 +217,21 @@ def main():
         for k in range(args.steps):
             m = tvf.momentum(k % n_inner + 1)
             evs[k][0].record(stream)
-            tvf.tv_fgp_step(b, p, r_cur, r_nxt, lam, m, variant=variant, z_ws=ws,
-                            stream=stream)
+            step(r_cur, r_nxt, m)
             evs[k][1].record(stream)
             r_cur, r_nxt = r_nxt, r_cur
         torch.cuda.synchronize()
         launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
 
     ms_per_step = region_ms / args.steps
-    step_bytes = BYTES_PER_VOXEL[args.variant] * nvox
+    step_bytes = (BYTES_PER_VOXEL_HALF if half else BYTES_PER_VOXEL[args.variant]) * nvox
     launch_avg_ms = float(np.mean(launch_ms))
     achieved = step_bytes / (launch_avg_ms * 1e-3) / 1e9
     region_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
 
-    # duality-gap reduction (reads b and p: 16 B per voxel)
+    # duality-gap reduction (reads b and p: 16 B per voxel), of the fp32 dual
+    if half:
+        p = p.float()
     gap_ws = torch.empty(tvf.gap_workspace_bytes(nx, ny, nz) // 8, dtype=torch.float64,
                          device=dev)
     gap_out = torch.empty(3, dtype=torch.float64, device=dev)
@@ -254,20 +280,26 @@ def main():
         threads = min(16, os.cpu_count() or 1)
         oracle.set_threads(threads)
         p0 = p0_host
-        cpu_outer = 10
+        cpu_outer = 1 if half else 10  # the half mode converts p, r every step: slower
+        if half:
+            p0 = oracle.f32_to_f16_bits(p0)
         t1 = time.perf_counter()
-        oracle.run(b_host, p0, p0, lam, cpu_outer, n_inner)
+        if half:
+            oracle.run_half(b_host, p0, p0, lam, cpu_outer, n_inner)
+        else:
+            oracle.run(b_host, p0, p0, lam, cpu_outer, n_inner)
         cpu_s = time.perf_counter() - t1
         cpu_steps = cpu_outer * n_inner
         cpu = {"value": round(cpu_s * 1e3 / cpu_steps, 3), "unit": "ms/step",
                "cores": oracle.get_threads(), "kind": "oracle",
                "sample": "first %d outer iterations (%d steps) of the same workload at "
-                         "full size, fp32 exact-order oracle, %.1f s" % (
-                             cpu_outer, cpu_steps, cpu_s)}
+                         "full size, fp32 exact-order oracle%s, %.1f s" % (
+                             cpu_outer, cpu_steps, " (binary16 dual)" if half else "",
+                             cpu_s)}
 
-    traffic = None if args.dims else measured_traffic(args.variant, args.workload)
+    traffic = None if (args.dims or half) else measured_traffic(args.variant, args.workload)
     out = {
-        "metric": METRIC,
+        "metric": METRIC if not half else METRIC.replace("fp32", "fp32 with binary16 p, r"),
         "value": round(ms_per_step, 5),
         "unit": "ms/step",
         "n_gpus": 1,
@@ -282,7 +314,8 @@ def main():
         "config": {"workload": phantoms.NAMES[args.workload] if not args.dims else
                    "%s recipe at %dx%dx%d" % (phantoms.NAMES[args.workload], nx, ny, nz),
                    "dims": [nx, ny, nz], "lambda": lam, "steps_per_outer": n_inner,
-                   "variant": args.variant, "parallelism": "single GPU"},
+                   "variant": args.variant, "dual_storage": "binary16" if half else "f32",
+                   "parallelism": "single GPU"},
         "gbps": round(region_gbs, 1),
         "pct_hbm_peak": round(100.0 * region_gbs / HBM_PEAK_GBS, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1),

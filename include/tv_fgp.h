@@ -134,6 +134,33 @@ int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
               int64_t nx, int64_t ny, int64_t nz, void *stream);
 
 /*
+ * One FGP step with the dual p and its momentum copy r stored as IEEE
+ * binary16 (the page "TV solver: the FGP step on the GPU" names a
+ * half-precision dual as a way to move fewer bytes, in its closing
+ * paragraph; the step itself is the one of section "What one step does").
+ * p, r_in, r_out are arrays of nx*ny*nz binary16 values (uint16_t bit
+ * patterns, 2-byte aligned); b is float.  Each value of p and r is widened to
+ * float exactly, the step is computed in float exactly as tv_fgp_step does,
+ * and the new p and r_out are rounded to binary16 (nearest, ties to even).
+ * 28 bytes per voxel instead of 52.  The result differs from the float
+ * dual; it is not an approximation of tv_fgp_step but its own iteration.
+ * Default kernel only.  Overlap rules and status codes as tv_fgp_step.
+ */
+int tv_fgp_step_h(const float *b, uint16_t *const p[3],
+                  const uint16_t *const r_in[3], uint16_t *const r_out[3],
+                  float lambda, float m, int64_t nx, int64_t ny, int64_t nz,
+                  void *stream);
+
+/* tv_fgp_run with the binary16 dual of tv_fgp_step_h (default kernel). */
+int tv_fgp_run_h(const float *b, uint16_t *const p[3], uint16_t *const r_a[3],
+                 uint16_t *const r_b[3], float lambda, int n_outer, int n_inner,
+                 int64_t nx, int64_t ny, int64_t nz, void *stream, int *r_final);
+
+/* tv_primal from a binary16 dual: z = max(b - lambda * L(p), 0) in float. */
+int tv_primal_h(const float *b, const uint16_t *const p[3], float *z, float lambda,
+                int64_t nx, int64_t ny, int64_t nz, void *stream);
+
+/*
  * Bytes of device workspace tv_fgp_duality_gap needs at these dimensions
  * (at most 24 KiB); 0 for invalid dimensions.
  */

@@ -173,7 +173,8 @@ void tv_oracle_f16_to_f32_array(const uint16_t *in, float *out, int64_t n)
  * FGP with the dual p and its momentum copy r stored in binary16, b in
  * binary32, arithmetic in binary32: every step widens p and r exactly, runs
  * the binary32 step (same code as tv_oracle_run_f32), and rounds the new p
- * and r to binary16 (nearest, ties to even).
+ * and r to binary16 (nearest, ties to even).  The conversions are element by
+ * element, so splitting them over threads does not change the result.
  */
 int tv_oracle_run_h(const float *b, uint16_t *p0, uint16_t *p1, uint16_t *p2,
                     uint16_t *r0, uint16_t *r1, uint16_t *r2, float lam,
@@ -192,6 +193,7 @@ int tv_oracle_run_h(const float *b, uint16_t *p0, uint16_t *p1, uint16_t *p2,
         for (int k = 1; k <= n_inner; ++k) {
             const float m = (float)tv_oracle_momentum(k);
             for (int a = 0; a < 3; ++a) {
+#pragma omp parallel for schedule(static)
                 for (int64_t i = 0; i < n; ++i) {
                     pf[a][i] = tv_oracle_f16_to_f32(ph[a][i]);
                     rf[a][i] = tv_oracle_f16_to_f32(rh[a][i]);
@@ -203,6 +205,7 @@ int tv_oracle_run_h(const float *b, uint16_t *p0, uint16_t *p1, uint16_t *p2,
                 return -1;
             }
             for (int a = 0; a < 3; ++a) {
+#pragma omp parallel for schedule(static)
                 for (int64_t i = 0; i < n; ++i) {
                     ph[a][i] = tv_oracle_f32_to_f16(pf[a][i]);
                     rh[a][i] = tv_oracle_f32_to_f16(rn[a][i]);

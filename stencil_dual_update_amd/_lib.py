@@ -31,7 +31,7 @@ VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
 
 # Names declared in include/tv_fgp.h, in declaration order.
 EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_primal",
-           "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
+           "tv_fgp_step_h", "tv_fgp_run_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
            "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_status_string",
            "tv_fgp_variant_name")
 
@@ -71,6 +71,13 @@ def _load():
                                ctypes.POINTER(ctypes.c_int)]
     lib.tv_primal.restype = ctypes.c_int
     lib.tv_primal.argtypes = [P, P3, P, F, I64, I64, I64, P]
+    lib.tv_fgp_step_h.restype = ctypes.c_int
+    lib.tv_fgp_step_h.argtypes = [P, P3, P3, P3, F, F, I64, I64, I64, P]
+    lib.tv_fgp_run_h.restype = ctypes.c_int
+    lib.tv_fgp_run_h.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int, I64, I64, I64,
+                                 P, ctypes.POINTER(ctypes.c_int)]
+    lib.tv_primal_h.restype = ctypes.c_int
+    lib.tv_primal_h.argtypes = [P, P3, P, F, I64, I64, I64, P]
     lib.tv_fgp_gap_workspace_bytes.restype = ctypes.c_size_t
     lib.tv_fgp_gap_workspace_bytes.argtypes = [I64, I64, I64]
     lib.tv_fgp_duality_gap.restype = ctypes.c_int
@@ -153,6 +160,29 @@ def _check_volume(t, shape, what):
         raise ValueError("%s must be contiguous" % what)
     if tuple(t.shape) != shape:
         raise ValueError("%s has shape %s, expected %s" % (what, tuple(t.shape), shape))
+
+
+def _check_half(t, shape, what):
+    if t is None or isinstance(t, int):
+        return
+    import torch
+    if not t.is_cuda or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous device tensor" % what)
+    if t.dtype not in (torch.float16, torch.int16):
+        raise ValueError("%s must hold binary16 values (float16 or int16 bit patterns)" % what)
+    if tuple(t.shape) != shape:
+        raise ValueError("%s has shape %s, expected %s" % (what, tuple(t.shape), shape))
+
+
+def _hfield(f, shape, what):
+    if f is None:
+        return (ctypes.c_void_p * 3)(None, None, None)
+    comps = [f[0], f[1], f[2]] if not isinstance(f, (list, tuple)) else list(f)
+    if len(comps) != 3:
+        raise ValueError("%s needs three components" % what)
+    for a, c in enumerate(comps):
+        _check_half(c, shape, "%s[%d]" % (what, a))
+    return (ctypes.c_void_p * 3)(*[_addr(c) for c in comps])
 
 
 def _field(f, shape, what):
@@ -287,3 +317,37 @@ def tv_fgp_solve(b, p, r_a, r_b, lam, max_outer, n_inner, tol, gap_ws, gap_dev,
                           ctypes.byref(done), host)
     _raise(st, "tv_fgp_solve")
     return done.value, where.value, (host[0], host[1], host[2])
+
+
+def tv_fgp_step_h(b, p, r_in, r_out, lam, m, stream=None, dims=None):
+    """One FGP step with p, r stored as binary16 (float16 tensors)."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    st = lib.tv_fgp_step_h(_addr(b), _hfield(p, shape, "p"), _hfield(r_in, shape, "r_in"),
+                           _hfield(r_out, shape, "r_out"), float(lam), float(m), nx, ny, nz,
+                           _stream(stream))
+    _raise(st, "tv_fgp_step_h")
+
+
+def tv_fgp_run_h(b, p, r_a, r_b, lam, n_outer, n_inner, stream=None, dims=None):
+    """tv_fgp_run with the binary16 dual; returns 0 if the last r is in r_a, 1 if in r_b."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    where = ctypes.c_int(-1)
+    st = lib.tv_fgp_run_h(_addr(b), _hfield(p, shape, "p"), _hfield(r_a, shape, "r_a"),
+                          _hfield(r_b, shape, "r_b"), float(lam), int(n_outer), int(n_inner),
+                          nx, ny, nz, _stream(stream), ctypes.byref(where))
+    _raise(st, "tv_fgp_run_h")
+    return where.value
+
+
+def tv_primal_h(b, p, z, lam, stream=None, dims=None):
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_volume(z, shape, "z")
+    st = lib.tv_primal_h(_addr(b), _hfield(p, shape, "p"), _addr(z), float(lam), nx, ny, nz,
+                         _stream(stream))
+    _raise(st, "tv_primal_h")

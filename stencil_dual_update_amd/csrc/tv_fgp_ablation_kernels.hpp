@@ -193,11 +193,12 @@ __global__ __launch_bounds__(kBlock) void fused_point_kernel(
 
 // --------------------------------------------------------------------------
 // Two-kernel ablation, part 1 (also the primal read-out): z = max(b - lam L(r), 0).
-// Each thread walks a column along z and carries r_z of the plane below.
-template <typename I>
+// Each thread walks a column along z and carries r_z of the plane below.  S
+// is the element type of r (float, or _Float16 for the half-storage dual).
+template <typename I, typename S = float>
 __global__ __launch_bounds__(kBlock) void primal_kernel(
-    const float *__restrict__ b, const float *__restrict__ ri0,
-    const float *__restrict__ ri1, const float *__restrict__ ri2,
+    const float *__restrict__ b, const S *__restrict__ ri0,
+    const S *__restrict__ ri1, const S *__restrict__ ri2,
     float *__restrict__ zout, float lam, Geometry<I> g) {
   const I lx = (I)(threadIdx.x % kTileX);
   const I ly = (I)(threadIdx.x / kTileX);
@@ -217,9 +218,10 @@ __global__ __launch_bounds__(kBlock) void primal_kernel(
     I i = x + sy * y + sz * z0;
     float r2_lo = load_or_zero(ri2, z0 > 0, i - sz, i);
     for (I zp = z0; zp < z1; ++zp, i += sz) {
-      const float r2c = ri2[i];
-      zout[i] = primal_z(b[i], ri0[i], load_or_zero(ri0, low_x, i - 1, i), ri1[i],
-                         load_or_zero(ri1, low_y, i - sy, i), r2c, r2_lo, lam);
+      const float r2c = (float)ri2[i];
+      zout[i] = primal_z(b[i], (float)ri0[i], load_or_zero(ri0, low_x, i - 1, i),
+                         (float)ri1[i], load_or_zero(ri1, low_y, i - sy, i), r2c,
+                         r2_lo, lam);
       r2_lo = r2c;
     }
   }

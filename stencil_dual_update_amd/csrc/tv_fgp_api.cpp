@@ -238,6 +238,124 @@ int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
   return launch_status(tvfgp::launch_primal(a));
 }
 
+// ---------------------------------------------------------------------------
+// dual stored as binary16
+
+static Buf hvol(const void *p, size_t half_bytes, bool written) {
+  return Buf{p, half_bytes, sizeof(uint16_t), written};
+}
+
+int tv_fgp_step_h(const float *b, uint16_t *const p[3],
+                  const uint16_t *const r_in[3], uint16_t *const r_out[3],
+                  float lambda, float m, int64_t nx, int64_t ny, int64_t nz,
+                  void *stream) {
+  if (p == nullptr || r_in == nullptr || r_out == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  if (!isfinite(m)) return TV_ERR_PARAM;
+  const size_t hb = bytes / 2;
+  const Buf bufs[10] = {vol(b, bytes, false),      hvol(p[0], hb, true),
+                        hvol(p[1], hb, true),      hvol(p[2], hb, true),
+                        hvol(r_in[0], hb, false),  hvol(r_in[1], hb, false),
+                        hvol(r_in[2], hb, false),  hvol(r_out[0], hb, true),
+                        hvol(r_out[1], hb, true),  hvol(r_out[2], hb, true)};
+  st = check_buffers(bufs, 10);
+  if (st != TV_OK) return st;
+  tvfgp::StepArgsH h;
+  h.b = b;
+  for (int k = 0; k < 3; ++k) {
+    h.p[k] = p[k];
+    h.r_in[k] = r_in[k];
+    h.r_out[k] = r_out[k];
+  }
+  h.lam = lambda;
+  h.c = c;
+  h.m = m;
+  h.nx = nx;
+  h.ny = ny;
+  h.nz = nz;
+  h.stream = stream;
+  return launch_status(tvfgp::launch_fused_zx_h(h));
+}
+
+int tv_fgp_run_h(const float *b, uint16_t *const p[3], uint16_t *const r_a[3],
+                 uint16_t *const r_b[3], float lambda, int n_outer, int n_inner,
+                 int64_t nx, int64_t ny, int64_t nz, void *stream, int *r_final) {
+  if (r_final) *r_final = 0;
+  if (p == nullptr || r_a == nullptr || r_b == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  if (n_outer < 0 || n_inner < 0) return TV_ERR_PARAM;
+  const size_t hb = bytes / 2;
+  const Buf bufs[10] = {vol(b, bytes, false),   hvol(p[0], hb, true),
+                        hvol(p[1], hb, true),   hvol(p[2], hb, true),
+                        hvol(r_a[0], hb, true), hvol(r_a[1], hb, true),
+                        hvol(r_a[2], hb, true), hvol(r_b[0], hb, true),
+                        hvol(r_b[1], hb, true), hvol(r_b[2], hb, true)};
+  st = check_buffers(bufs, 10);
+  if (st != TV_OK) return st;
+  tvfgp::StepArgsH h;
+  h.b = b;
+  for (int k = 0; k < 3; ++k) h.p[k] = p[k];
+  h.lam = lambda;
+  h.c = c;
+  h.nx = nx;
+  h.ny = ny;
+  h.nz = nz;
+  h.stream = stream;
+  int where = 0;
+  for (int o = 0; o < n_outer; ++o) {
+    double t = 1.0;
+    for (int k = 1; k <= n_inner; ++k) {
+      const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
+      h.m = (float)((t - 1.0) / t_next);
+      t = t_next;
+      uint16_t *const *in = where ? r_b : r_a;
+      uint16_t *const *out = where ? r_a : r_b;
+      for (int a = 0; a < 3; ++a) {
+        h.r_in[a] = in[a];
+        h.r_out[a] = out[a];
+      }
+      if (tvfgp::launch_fused_zx_h(h) != 0) return TV_ERR_LAUNCH;
+      where ^= 1;
+      if (r_final) *r_final = where;
+    }
+  }
+  return TV_OK;
+}
+
+int tv_primal_h(const float *b, const uint16_t *const p[3], float *z, float lambda,
+                int64_t nx, int64_t ny, int64_t nz, void *stream) {
+  if (p == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  const size_t hb = bytes / 2;
+  const Buf bufs[5] = {vol(b, bytes, false), hvol(p[0], hb, false),
+                       hvol(p[1], hb, false), hvol(p[2], hb, false),
+                       vol(z, bytes, true)};
+  st = check_buffers(bufs, 5);
+  if (st != TV_OK) return st;
+  tvfgp::PrimalArgsH a;
+  a.b = b;
+  for (int k = 0; k < 3; ++k) a.p[k] = p[k];
+  a.z = z;
+  a.lam = lambda;
+  a.nx = nx;
+  a.ny = ny;
+  a.nz = nz;
+  a.stream = stream;
+  return launch_status(tvfgp::launch_primal_h(a));
+}
+
 size_t tv_fgp_gap_workspace_bytes(int64_t nx, int64_t ny, int64_t nz) {
   if (volume_bytes(nx, ny, nz) == 0) return 0;
   return gap_ws_bytes(nx, ny, nz);

@@ -103,12 +103,13 @@ __device__ __forceinline__ void dual_update(float zi, float zx, float zy,
   p2 = pz;
 }
 
-// Load src[cond ? idx : alt] and return it if cond, else +0.  Both indices
-// must be in bounds; the address is clamped instead of branching.
-template <typename I>
-__device__ __forceinline__ float load_or_zero(const float *__restrict__ src,
+// Load src[cond ? idx : alt] (widened to float) and return it if cond, else
+// +0.  Both indices must be in bounds; the address is clamped instead of
+// branching.
+template <typename T, typename I>
+__device__ __forceinline__ float load_or_zero(const T *__restrict__ src,
                                               bool cond, I idx, I alt) {
-  const float v = src[cond ? idx : alt];
+  const float v = (float)src[cond ? idx : alt];
   return cond ? v : 0.0f;
 }
 

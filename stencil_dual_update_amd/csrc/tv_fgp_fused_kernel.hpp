@@ -77,6 +77,28 @@ __device__ __forceinline__ void st_stream(float *__restrict__ base, Off off,
   __builtin_nontemporal_store(v, (float *)((char *)base + off));
 }
 
+// Loads and stores of the dual volumes, whose element type S is float or
+// _Float16.  Offsets are kept in bytes of a float volume (4 per element); a
+// volume of S elements is addressed at offset * sizeof(S) / 4.  Values are
+// widened to float on load (exact) and rounded to S on store (nearest, ties
+// to even).
+template <typename S, typename Off>
+__device__ __forceinline__ const S *sptr(const S *base, Off off) {
+  return (const S *)((const char *)base + off / (Off)(4 / sizeof(S)));
+}
+template <typename S, typename Off>
+__device__ __forceinline__ float lds(const S *__restrict__ base, Off off) {
+  return (float)*sptr(base, off);
+}
+template <typename S, typename Off>
+__device__ __forceinline__ float lds_stream(const S *__restrict__ base, Off off) {
+  return (float)__builtin_nontemporal_load(sptr(base, off));
+}
+template <typename S, typename Off>
+__device__ __forceinline__ void sts_stream(S *__restrict__ base, Off off, float v) {
+  __builtin_nontemporal_store((S)v, (S *)sptr((const S *)base, off));
+}
+
 // Tile t (after the XCD mapping) -> (tx, ty, tz).  Order, slowest first:
 // group of tile columns, band of tile rows, z, row within the band, column
 // within the group.  The last group and the last band may be narrower.
@@ -99,13 +121,12 @@ __device__ __forceinline__ void ordered_tile(I t, const ZxGeometry<I, Off> &g,
   tx = x_lo + rem % width;
 }
 
-template <typename I, typename Off, bool kStreamP>
+template <typename I, typename Off, bool kStreamP, typename S>
 __global__ __launch_bounds__(kZxBlock) void fused_zx_kernel(
-    const float *__restrict__ b, float *__restrict__ p0,
-    float *__restrict__ p1, float *__restrict__ p2,
-    const float *__restrict__ ri0, const float *__restrict__ ri1,
-    const float *__restrict__ ri2, float *__restrict__ ro0,
-    float *__restrict__ ro1, float *__restrict__ ro2, float lam, float c,
+    const float *__restrict__ b, S *__restrict__ p0, S *__restrict__ p1,
+    S *__restrict__ p2, const S *__restrict__ ri0, const S *__restrict__ ri1,
+    const S *__restrict__ ri2, S *__restrict__ ro0, S *__restrict__ ro1,
+    S *__restrict__ ro2, float lam, float c,
     float m, ZxGeometry<I, Off> g) {
   constexpr int kW = kZxTileX + 1, kH = kZxTileY + 1;
   __shared__ float zring[3][kH][kW];
@@ -145,23 +166,23 @@ __global__ __launch_bounds__(kZxBlock) void fused_zx_kernel(
     // z at plane z0, and the carried r of the column
     float r0c = 0.0f, r1c = 0.0f, r2c = 0.0f, r2h = 0.0f, zc = 0.0f;
     if (own_ok) {
-      r0c = ld(ri0, oi);
-      r1c = ld(ri1, oi);
-      r2c = ld(ri2, oi);
-      const float a = ld(ri0, low_x ? oi - four : oi);
-      const float e = ld(ri1, low_y ? oi - sy4 : oi);
-      const float f = ld(ri2, low_z ? oi - sz4 : oi);
+      r0c = lds(ri0, oi);
+      r1c = lds(ri1, oi);
+      r2c = lds(ri2, oi);
+      const float a = lds(ri0, low_x ? oi - four : oi);
+      const float e = lds(ri1, low_y ? oi - sy4 : oi);
+      const float f = lds(ri2, low_z ? oi - sz4 : oi);
       zc = primal_z(ld(b, oi), r0c, low_x ? a : 0.0f, r1c, low_y ? e : 0.0f,
                     r2c, low_z ? f : 0.0f, lam);
       zring[0][ly][lx] = zc;
     }
     if (halo_ok) {
-      r2h = ld(ri2, oh);
-      const float a = ld(ri0, hlow_x ? oh - four : oh);
-      const float e = ld(ri1, hlow_y ? oh - sy4 : oh);
-      const float f = ld(ri2, low_z ? oh - sz4 : oh);
+      r2h = lds(ri2, oh);
+      const float a = lds(ri0, hlow_x ? oh - four : oh);
+      const float e = lds(ri1, hlow_y ? oh - sy4 : oh);
+      const float f = lds(ri2, low_z ? oh - sz4 : oh);
       zring[0][hyl][hxl] =
-          primal_z(ld(b, oh), ld(ri0, oh), hlow_x ? a : 0.0f, ld(ri1, oh),
+          primal_z(ld(b, oh), lds(ri0, oh), hlow_x ? a : 0.0f, lds(ri1, oh),
                    hlow_y ? e : 0.0f, r2h, low_z ? f : 0.0f, lam);
     }
 
@@ -173,20 +194,20 @@ __global__ __launch_bounds__(kZxBlock) void fused_zx_kernel(
       if (own_ok) {
         const Off j = oi + dz;
         nb = ld(b, j);
-        n0 = ld(ri0, j);
-        n1 = ld(ri1, j);
-        n2 = ld(ri2, j);
-        n0l = ld(ri0, low_x ? j - four : j);
-        n1l = ld(ri1, low_y ? j - sy4 : j);
+        n0 = lds(ri0, j);
+        n1 = lds(ri1, j);
+        n2 = lds(ri2, j);
+        n0l = lds(ri0, low_x ? j - four : j);
+        n1l = lds(ri1, low_y ? j - sy4 : j);
       }
       if (halo_ok) {
         const Off j = oh + dz;
         hb = ld(b, j);
-        h0 = ld(ri0, j);
-        h1 = ld(ri1, j);
-        h2 = ld(ri2, j);
-        h0l = ld(ri0, hlow_x ? j - four : j);
-        h1l = ld(ri1, hlow_y ? j - sy4 : j);
+        h0 = lds(ri0, j);
+        h1 = lds(ri1, j);
+        h2 = lds(ri2, j);
+        h0l = lds(ri0, hlow_x ? j - four : j);
+        h1l = lds(ri1, hlow_y ? j - sy4 : j);
       }
     };
     if (z0 + 1 < g.nz) load_plane(z0 + 1);
@@ -198,9 +219,9 @@ __global__ __launch_bounds__(kZxBlock) void fused_zx_kernel(
       const Off ok = oi + (Off)(k - z0) * sz4;
       float pv0 = 0.0f, pv1 = 0.0f, pv2 = 0.0f;
       if (own_ok) {
-        pv0 = kStreamP ? ld_stream(p0, ok) : ld(p0, ok);
-        pv1 = kStreamP ? ld_stream(p1, ok) : ld(p1, ok);
-        pv2 = kStreamP ? ld_stream(p2, ok) : ld(p2, ok);
+        pv0 = kStreamP ? lds_stream(p0, ok) : lds(p0, ok);
+        pv1 = kStreamP ? lds_stream(p1, ok) : lds(p1, ok);
+        pv2 = kStreamP ? lds_stream(p2, ok) : lds(p2, ok);
       }
       // plane k+1 values in hand; start the loads of plane k+2
       const float cb = nb, c0 = n0, c1 = n1, c2 = n2, c0l = n0l, c1l = n1l;
@@ -229,12 +250,12 @@ __global__ __launch_bounds__(kZxBlock) void fused_zx_kernel(
         float o0, o1, o2;
         dual_update(zc, zx, zy, zz, has_x, has_y, has_z, r0c, r1c, r2c, pv0,
                     pv1, pv2, c, m, o0, o1, o2);
-        st_stream(p0, ok, pv0);
-        st_stream(p1, ok, pv1);
-        st_stream(p2, ok, pv2);
-        st_stream(ro0, ok, o0);
-        st_stream(ro1, ok, o1);
-        st_stream(ro2, ok, o2);
+        sts_stream(p0, ok, pv0);
+        sts_stream(p1, ok, pv1);
+        sts_stream(p2, ok, pv2);
+        sts_stream(ro0, ok, o0);
+        sts_stream(ro1, ok, o1);
+        sts_stream(ro2, ok, o2);
       }
       zc = zz;
       r0c = c0;

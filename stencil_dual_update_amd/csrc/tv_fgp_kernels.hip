@@ -60,7 +60,22 @@ int launch_primal_t(const PrimalArgs &a) {
   return hipGetLastError() == hipSuccess ? 0 : kLaunchFailed;
 }
 
+template <typename I>
+int launch_primal_h_t(const PrimalArgsH &a) {
+  const Geometry<I> g = make_geometry<I>(a.nx, a.ny, a.nz, kDefaultPlanes);
+  primal_kernel<I, _Float16><<<grid_for(g.ntiles), dim3(kBlock), 0,
+                               (hipStream_t)a.stream>>>(
+      a.b, (const _Float16 *)a.p[0], (const _Float16 *)a.p[1],
+      (const _Float16 *)a.p[2], a.z, a.lam, g);
+  return hipGetLastError() == hipSuccess ? 0 : kLaunchFailed;
+}
+
 }  // namespace
+
+int launch_primal_h(const PrimalArgsH &a) {
+  return fits_int32(a.nx, a.ny, a.nz) ? launch_primal_h_t<int32_t>(a)
+                                      : launch_primal_h_t<int64_t>(a);
+}
 
 int launch_step(const StepArgs &a) {
   return fits_int32(a.nx, a.ny, a.nz) ? launch_step_t<int32_t>(a)

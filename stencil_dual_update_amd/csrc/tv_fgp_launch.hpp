@@ -46,6 +46,27 @@ struct PrimalArgs {
   void *stream;
 };
 
+// Step with the dual stored as binary16 (default kernel only).  The 16-bit
+// pointers hold IEEE binary16 values.
+struct StepArgsH {
+  const float *b;
+  uint16_t *p[3];
+  const uint16_t *r_in[3];
+  uint16_t *r_out[3];
+  float lam, c, m;
+  int64_t nx, ny, nz;
+  void *stream;
+};
+
+struct PrimalArgsH {
+  const float *b;
+  const uint16_t *p[3];
+  float *z;
+  float lam;
+  int64_t nx, ny, nz;
+  void *stream;
+};
+
 struct GapArgs {
   const float *b;
   const float *p[3];
@@ -62,6 +83,8 @@ int launch_step(const StepArgs &a);
 int launch_primal(const PrimalArgs &a);
 int launch_lds_march(const StepArgs &a);
 int launch_fused_zx(const StepArgs &a);
+int launch_fused_zx_h(const StepArgsH &a);
+int launch_primal_h(const PrimalArgsH &a);
 // Duality gap of p (two kernels: partial sums, then their fixed-order sum).
 int launch_duality_gap(const GapArgs &a);
 // Partial triples the gap reduction writes for these dimensions.

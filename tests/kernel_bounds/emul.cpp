@@ -9,7 +9,8 @@
 // checked here (barriers are no-ops), only addresses.
 //
 // usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
-//   variant: fused | fused_nostream | reg_march | point | two_kernel | lds_march | primal | gap
+//   variant: fused | fused_nostream | fused_h | fused_nostream_h | reg_march | point |
+//            two_kernel | lds_march | primal | primal_h | gap
 //   wide: 1 instantiates the 64-bit offset / index path regardless of size
 #include <stdio.h>
 #include <stdlib.h>
@@ -74,22 +75,26 @@ struct Bufs {
   float *b, *p[3], *ri[3], *ro[3], *z;
 };
 
-template <typename I, typename Off>
+template <typename I, typename Off, typename S>
 void run_fused(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid,
                bool stream_p) {
   const auto g = tvfgp::zx_geometry<I, Off>(nx, ny, nz);
   const unsigned gr = pick_grid(g.ntiles, grid);
+  S *p[3], *ri[3], *ro[3];
+  for (int a = 0; a < 3; ++a) {
+    p[a] = (S *)v.p[a];
+    ri[a] = (S *)v.ri[a];
+    ro[a] = (S *)v.ro[a];
+  }
   if (stream_p)
     run_grid(gr, tvfgp::kZxBlock, [&] {
-      tvfgp::fused_zx_kernel<I, Off, true>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1],
-                                           v.ri[2], v.ro[0], v.ro[1], v.ro[2], 0.01f,
-                                           8.3f, 0.5f, g);
+      tvfgp::fused_zx_kernel<I, Off, true, S>(v.b, p[0], p[1], p[2], ri[0], ri[1], ri[2],
+                                              ro[0], ro[1], ro[2], 0.01f, 8.3f, 0.5f, g);
     });
   else
     run_grid(gr, tvfgp::kZxBlock, [&] {
-      tvfgp::fused_zx_kernel<I, Off, false>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1],
-                                            v.ri[2], v.ro[0], v.ro[1], v.ro[2], 0.01f,
-                                            8.3f, 0.5f, g);
+      tvfgp::fused_zx_kernel<I, Off, false, S>(v.b, p[0], p[1], p[2], ri[0], ri[1], ri[2],
+                                               ro[0], ro[1], ro[2], 0.01f, 8.3f, 0.5f, g);
     });
 }
 
@@ -108,6 +113,12 @@ void run_ablation(const char *variant, const Bufs &v, int64_t nx, int64_t ny, in
     run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
       fused_point_kernel<I>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2],
                             v.ro[0], v.ro[1], v.ro[2], 0.01f, 8.3f, 0.5f, g);
+    });
+  } else if (!strcmp(variant, "primal_h")) {
+    const Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
+    run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
+      primal_kernel<I, _Float16>(v.b, (const _Float16 *)v.ri[0], (const _Float16 *)v.ri[1],
+                                 (const _Float16 *)v.ri[2], v.z, 0.01f, g);
     });
   } else if (!strcmp(variant, "two_kernel") || !strcmp(variant, "primal")) {
     const Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
@@ -154,21 +165,30 @@ int main(int argc, char **argv) {
   const bool end_aligned = atoi(argv[7]) != 0;
   const int64_t planes = atoll(argv[8]);
   const size_t bytes = (size_t)(nx * ny * nz) * sizeof(float);
+  // dual volumes of the binary16 variants are half as long
+  const bool half = strstr(variant, "_h") != nullptr;
+  const size_t dbytes = half ? bytes / 2 : bytes;
   Bufs v;
   unsigned seed = 1;
   v.b = guarded(bytes, end_aligned, seed++);
   for (int a = 0; a < 3; ++a) {
-    v.p[a] = guarded(bytes, end_aligned, seed++);
-    v.ri[a] = guarded(bytes, end_aligned, seed++);
-    v.ro[a] = guarded(bytes, end_aligned, seed++);
+    v.p[a] = guarded(dbytes, end_aligned, seed++);
+    v.ri[a] = guarded(dbytes, end_aligned, seed++);
+    v.ro[a] = guarded(dbytes, end_aligned, seed++);
   }
   v.z = guarded(bytes, end_aligned, seed++);
   if (!strcmp(variant, "fused") || !strcmp(variant, "fused_nostream")) {
     const bool sp = !strcmp(variant, "fused");
     if (wide)
-      run_fused<int64_t, uint64_t>(v, nx, ny, nz, grid, sp);
+      run_fused<int64_t, uint64_t, float>(v, nx, ny, nz, grid, sp);
     else
-      run_fused<int32_t, uint32_t>(v, nx, ny, nz, grid, sp);
+      run_fused<int32_t, uint32_t, float>(v, nx, ny, nz, grid, sp);
+  } else if (!strcmp(variant, "fused_h") || !strcmp(variant, "fused_nostream_h")) {
+    const bool sp = !strcmp(variant, "fused_h");
+    if (wide)
+      run_fused<int64_t, uint64_t, _Float16>(v, nx, ny, nz, grid, sp);
+    else
+      run_fused<int32_t, uint32_t, _Float16>(v, nx, ny, nz, grid, sp);
   } else if (wide) {
     run_ablation<int64_t>(variant, v, nx, ny, nz, grid, planes);
   } else {

@@ -265,3 +265,45 @@ def test_solve_rejects(kw, code):
     st, where, done = solve(**kw)
     assert st == code
     assert where == 0 and done == 0
+
+
+def step_h(b=0, p=(1, 2, 3), ri=(4, 5, 6), ro=(7, 8, 9), lam=0.01, m=0.0, dims=(NX, NY, NZ),
+           pp=None):
+    return L.tv_fgp_step_h(None if b is None else addr(b), pp or field(*p), field(*ri),
+                           field(*ro), lam, m, *dims, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=None), tvf.TV_ERR_NULL),
+    (dict(p=(1, None, 3)), tvf.TV_ERR_NULL),
+    (dict(dims=(0, NY, NZ)), tvf.TV_ERR_DIMS),
+    (dict(lam=0.0), tvf.TV_ERR_PARAM),
+    (dict(m=float("nan")), tvf.TV_ERR_PARAM),
+    (dict(ro=(7, 8, 5)), tvf.TV_ERR_ALIAS),
+    (dict(p=(1, 2, 0)), tvf.TV_ERR_ALIAS),
+])
+def test_step_h_rejects(kw, code):
+    assert step_h(**kw) == code
+
+
+def test_step_h_half_sized_buffers():
+    # binary16 volumes are half as long: a p component that starts inside the
+    # second half of a float-sized slot overlaps nothing
+    vol_h = NX * NY * NZ * 2
+    pp = P3(addr(1), addr(1) + vol_h, addr(2))
+    ro = P3(addr(7), addr(8), addr(7) + vol_h)
+    assert L.tv_fgp_run_h(addr(0), pp, field(4, 5, 6), ro, 0.01, 0, 10, NX, NY, NZ, None,
+                          None) == tvf.TV_OK
+    pp_bad = P3(addr(1), addr(1) + vol_h - 2, addr(2))  # one element of overlap
+    assert L.tv_fgp_run_h(addr(0), pp_bad, field(4, 5, 6), field(7, 8, 9), 0.01, 0, 10,
+                          NX, NY, NZ, None, None) == tvf.TV_ERR_ALIAS
+    pp_odd = P3(addr(1) + 1, addr(2), addr(3))
+    assert L.tv_fgp_run_h(addr(0), pp_odd, field(4, 5, 6), field(7, 8, 9), 0.01, 0, 10,
+                          NX, NY, NZ, None, None) == tvf.TV_ERR_ALIGN
+
+
+def test_primal_h_rejects():
+    assert L.tv_primal_h(addr(0), field(1, 2, 3), addr(1), 0.01, NX, NY, NZ, None) \
+        == tvf.TV_ERR_ALIAS
+    assert L.tv_primal_h(addr(0), field(1, 2, 3), None, 0.01, NX, NY, NZ, None) \
+        == tvf.TV_ERR_NULL

@@ -22,8 +22,8 @@ CSRC = os.path.join(ROOT, "stencil_dual_update_amd", "csrc")
 SHAPES = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70), (65, 5, 17),
           (63, 3, 2), (2, 2, 2), (64, 8, 4), (64, 8, 5), (64, 4, 16), (128, 16, 8),
           (1100, 10, 7), (2100, 20, 5), (3, 300, 5), (200, 9, 33)]
-VARIANTS = ["fused", "fused_nostream", "reg_march", "point", "two_kernel", "lds_march", "primal",
-            "gap"]
+VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "reg_march", "point",
+            "two_kernel", "lds_march", "primal", "primal_h", "gap"]
 
 
 def compiler():
@@ -49,7 +49,8 @@ def test_every_access_in_bounds(emul, variant):
         for wide in (0, 1):
             for end in (0, 1):
                 for grid in ((0, 7) if wide else (0,)):
-                    for planes in ((8, 3) if variant not in ("fused", "fused_nostream", "point", "gap")
+                    for planes in ((8, 3) if variant not in ("fused", "fused_nostream", "fused_h",
+                                                             "fused_nostream_h", "point", "gap")
                                    else (4,)):
                         args = [emul, variant, str(nx), str(ny), str(nz), str(wide), str(grid),
                                 str(end), str(planes)]
