@@ -37,7 +37,7 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
-BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "reg_march": 52,
+BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "reg_march": 52, "pair": 52,
                    "two_kernel": 72}
 BYTES_PER_VOXEL_HALF = 28
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_512.json")

@@ -69,6 +69,10 @@ extern "C" {
 #define TV_FGP_REG_MARCH  4  /* ablation: each thread walks a column along z,
                                 carries its own z and r in registers and recomputes
                                 z at the +x and +y neighbours                        */
+#define TV_FGP_PAIR       5  /* the fused march with two x-adjacent voxels per lane
+                                (128x8 tiles, pair loads and stores) where nx is even
+                                and every volume is aligned to two elements; the
+                                fused kernel otherwise                               */
 
 /*
  * One FGP step ("TV solver: the FGP step on the GPU", section "What one step
@@ -144,14 +148,16 @@ int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
  * and the new p and r_out are rounded to binary16 (nearest, ties to even).
  * 28 bytes per voxel instead of 52.  The result differs from the float
  * dual; it is not an approximation of tv_fgp_step but its own iteration.
- * Default kernel only.  Overlap rules and status codes as tv_fgp_step.
+ * Kernel: the two-voxels-per-lane march of TV_FGP_PAIR when nx is even and
+ * every volume is 4-byte aligned, the fused one-voxel march otherwise (same
+ * bits either way).  Overlap rules and status codes as tv_fgp_step.
  */
 int tv_fgp_step_h(const float *b, uint16_t *const p[3],
                   const uint16_t *const r_in[3], uint16_t *const r_out[3],
                   float lambda, float m, int64_t nx, int64_t ny, int64_t nz,
                   void *stream);
 
-/* tv_fgp_run with the binary16 dual of tv_fgp_step_h (default kernel). */
+/* tv_fgp_run with the binary16 dual of tv_fgp_step_h (same kernel choice). */
 int tv_fgp_run_h(const float *b, uint16_t *const p[3], uint16_t *const r_a[3],
                  uint16_t *const r_b[3], float lambda, int n_outer, int n_inner,
                  int64_t nx, int64_t ny, int64_t nz, void *stream, int *r_final);

@@ -26,8 +26,9 @@ LDS_MARCH = 1
 TWO_KERNEL = 2
 POINT = 3
 REG_MARCH = 4
+PAIR = 5
 VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
-            "point": POINT, "reg_march": REG_MARCH}
+            "point": POINT, "reg_march": REG_MARCH, "pair": PAIR}
 
 # Names declared in include/tv_fgp.h, in declaration order.
 EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_primal",

@@ -278,7 +278,7 @@ int tv_fgp_step_h(const float *b, uint16_t *const p[3],
   h.ny = ny;
   h.nz = nz;
   h.stream = stream;
-  return launch_status(tvfgp::launch_fused_zx_h(h));
+  return launch_status(tvfgp::launch_fused_pair_h(h));
 }
 
 int tv_fgp_run_h(const float *b, uint16_t *const p[3], uint16_t *const r_a[3],
@@ -322,7 +322,7 @@ int tv_fgp_run_h(const float *b, uint16_t *const p[3], uint16_t *const r_a[3],
         h.r_in[a] = in[a];
         h.r_out[a] = out[a];
       }
-      if (tvfgp::launch_fused_zx_h(h) != 0) return TV_ERR_LAUNCH;
+      if (tvfgp::launch_fused_pair_h(h) != 0) return TV_ERR_LAUNCH;
       where ^= 1;
       if (r_final) *r_final = where;
     }
@@ -489,6 +489,7 @@ const char *tv_fgp_variant_name(int variant) {
     case tvfgp::kVariantTwoKernel: return "two_kernel";
     case tvfgp::kVariantPoint: return "point";
     case tvfgp::kVariantRegMarch: return "reg_march";
+    case tvfgp::kVariantPair: return "pair";
     default: return nullptr;
   }
 }

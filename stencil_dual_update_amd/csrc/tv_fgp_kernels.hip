@@ -45,6 +45,8 @@ int launch_step_t(const StepArgs &a) {
     }
     case kVariantLdsMarch:
       return launch_lds_march(a);
+    case kVariantPair:
+      return launch_fused_pair(a);
     default:
       return kLaunchFailed;
   }

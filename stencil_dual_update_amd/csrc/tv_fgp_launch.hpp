@@ -13,7 +13,8 @@ constexpr int kVariantLdsMarch = 1;
 constexpr int kVariantTwoKernel = 2;
 constexpr int kVariantPoint = 3;
 constexpr int kVariantRegMarch = 4;
-constexpr int kNumVariants = 5;
+constexpr int kVariantPair = 5;
+constexpr int kNumVariants = 6;
 
 constexpr int kLaunchFailed = -1;
 
@@ -84,6 +85,10 @@ int launch_primal(const PrimalArgs &a);
 int launch_lds_march(const StepArgs &a);
 int launch_fused_zx(const StepArgs &a);
 int launch_fused_zx_h(const StepArgsH &a);
+// Two voxels per lane where nx is even and the volumes are aligned to two
+// elements; otherwise the one-voxel kernel above.
+int launch_fused_pair(const StepArgs &a);
+int launch_fused_pair_h(const StepArgsH &a);
 int launch_primal_h(const PrimalArgsH &a);
 // Duality gap of p (two kernels: partial sums, then their fixed-order sum).
 int launch_duality_gap(const GapArgs &a);

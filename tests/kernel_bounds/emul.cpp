@@ -9,8 +9,10 @@
 // checked here (barriers are no-ops), only addresses.
 //
 // usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
-//   variant: fused | fused_nostream | fused_h | fused_nostream_h | reg_march | point |
-//            two_kernel | lds_march | primal | primal_h | gap
+//   variant: fused | fused_nostream | fused_h | fused_nostream_h | pair | pair_nostream |
+//            pair_h | pair_nostream_h | reg_march | point | two_kernel | lds_march |
+//            primal | primal_h | gap
+//   (the pair variants need an even nx; with an odd one they report "ok" without running)
 //   wide: 1 instantiates the 64-bit offset / index path regardless of size
 #include <stdio.h>
 #include <stdlib.h>
@@ -22,6 +24,7 @@
 #include "tv_fgp_fused_kernel.hpp"
 #include "tv_fgp_gap_kernel.hpp"
 #include "tv_fgp_lds_kernel.hpp"
+#include "tv_fgp_pair_kernel.hpp"
 
 thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
 
@@ -74,6 +77,29 @@ unsigned pick_grid(int64_t ntiles, unsigned override_grid) {
 struct Bufs {
   float *b, *p[3], *ri[3], *ro[3], *z;
 };
+
+template <typename I, typename Off, typename S>
+void run_pair(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid,
+              bool stream_p) {
+  const auto g = tvfgp::pair_geometry<I, Off>(nx, ny, nz);
+  const unsigned gr = pick_grid(g.ntiles, grid);
+  S *p[3], *ri[3], *ro[3];
+  for (int a = 0; a < 3; ++a) {
+    p[a] = (S *)v.p[a];
+    ri[a] = (S *)v.ri[a];
+    ro[a] = (S *)v.ro[a];
+  }
+  if (stream_p)
+    run_grid(gr, tvfgp::kPairBlock, [&] {
+      tvfgp::fused_pair_kernel<I, Off, true, S>(v.b, p[0], p[1], p[2], ri[0], ri[1], ri[2],
+                                                ro[0], ro[1], ro[2], 0.01f, 8.3f, 0.5f, g);
+    });
+  else
+    run_grid(gr, tvfgp::kPairBlock, [&] {
+      tvfgp::fused_pair_kernel<I, Off, false, S>(v.b, p[0], p[1], p[2], ri[0], ri[1], ri[2],
+                                                 ro[0], ro[1], ro[2], 0.01f, 8.3f, 0.5f, g);
+    });
+}
 
 template <typename I, typename Off, typename S>
 void run_fused(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid,
@@ -183,6 +209,23 @@ int main(int argc, char **argv) {
       run_fused<int64_t, uint64_t, float>(v, nx, ny, nz, grid, sp);
     else
       run_fused<int32_t, uint32_t, float>(v, nx, ny, nz, grid, sp);
+  } else if (!strncmp(variant, "pair", 4)) {
+    const bool sp = strstr(variant, "nostream") == nullptr;
+    if (nx % 2 != 0) {
+      printf("ok %s skipped: nx odd\n", variant);
+      return 0;
+    }
+    if (half) {
+      if (wide)
+        run_pair<int64_t, uint64_t, _Float16>(v, nx, ny, nz, grid, sp);
+      else
+        run_pair<int32_t, uint32_t, _Float16>(v, nx, ny, nz, grid, sp);
+    } else {
+      if (wide)
+        run_pair<int64_t, uint64_t, float>(v, nx, ny, nz, grid, sp);
+      else
+        run_pair<int32_t, uint32_t, float>(v, nx, ny, nz, grid, sp);
+    }
   } else if (!strcmp(variant, "fused_h") || !strcmp(variant, "fused_nostream_h")) {
     const bool sp = !strcmp(variant, "fused_h");
     if (wide)

@@ -117,7 +117,7 @@ def test_workspace_bytes():
     (dict(lam=1e-45), tvf.TV_ERR_PARAM),           # 1/(12 lambda) overflows
     (dict(m=float("nan")), tvf.TV_ERR_PARAM),
     (dict(m=float("inf")), tvf.TV_ERR_PARAM),
-    (dict(variant=5), tvf.TV_ERR_VARIANT),
+    (dict(variant=6), tvf.TV_ERR_VARIANT),
     (dict(variant=-1), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),       # two-kernel without z
     (dict(variant=2, ws=0), tvf.TV_ERR_ALIAS),     # workspace aliases b
@@ -167,7 +167,7 @@ def run(b=0, p=(1, 2, 3), ra=(4, 5, 6), rb=(7, 8, 9), lam=0.01, n_outer=2, n_inn
     (dict(rb=(7, 8, 4)), tvf.TV_ERR_ALIAS),        # r_b aliases r_a
     (dict(ra=(4, 5, 1)), tvf.TV_ERR_ALIAS),        # r_a aliases p
     (dict(dims=(NX, NY, -4)), tvf.TV_ERR_DIMS),
-    (dict(variant=5), tvf.TV_ERR_VARIANT),
+    (dict(variant=6), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),
 ])
 def test_run_rejects(kw, code):

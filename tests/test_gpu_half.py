@@ -73,8 +73,10 @@ def test_run_half_matches_oracle(tvf, workload, n_outer, n_inner):
     assert np.array_equal(z.cpu().numpy().view(np.uint32), ze.view(np.uint32))
 
 
+# odd nx takes the one-voxel kernel, even nx the two-voxel one
 RAGGED = [(1, 1, 1), (2, 1, 1), (1, 1, 7), (63, 9, 5), (64, 8, 4), (65, 9, 5), (67, 45, 29),
-          (130, 3, 70), (1, 130, 3), (129, 1, 9), (1000, 7, 3), (33, 17, 1)]
+          (130, 3, 70), (1, 130, 3), (129, 1, 9), (1000, 7, 3), (33, 17, 1), (258, 17, 6),
+          (126, 9, 4), (128, 8, 4), (2, 5, 9)]
 
 
 @pytest.mark.parametrize("dims", RAGGED, ids=lambda d: "x".join(map(str, d)))
@@ -159,3 +161,36 @@ def test_half_nan_input(tvf):
     assert np.array_equal(nan_e & ((pe & 0x3FF) != 0), nan_g & ((pg & 0x3FF) != 0))
     keep = ~(nan_e | nan_g)
     assert np.array_equal(pg[keep], pe[keep])
+
+
+@pytest.mark.parametrize("dims,guard", [((67, 9, 18), 4096), ((130, 9, 18), 4096),
+                                        ((130, 9, 18), 4097)],
+                         ids=["nx67", "nx130", "nx130_odd_offset"])
+def test_half_nan_guard_bands(tvf, dims, guard):
+    """binary16 volumes between NaN guard bands: no write may touch them, no
+    read of them may reach a result.  An odd guard length leaves the volumes
+    aligned to one element but not two."""
+    nx, ny, nz = dims
+    n = nx * ny * nz
+    b, p0, r0 = half_inputs(4, dims)
+    pe, re = oracle.run_half(b, p0, r0, 0.003, 1, 6)
+    store = torch.full((9, n + 2 * guard), float("nan"), dtype=torch.float16, device="cuda")
+
+    def vol(k, init=None):
+        t = store[k, guard:guard + n].view(nz, ny, nx)
+        if init is not None:
+            t.copy_(to_dev_half(init))
+        return t
+
+    bt = torch.from_numpy(b).to("cuda")
+    p = [vol(a, p0[a]) for a in range(3)]
+    ra = [vol(3 + a, r0[a]) for a in range(3)]
+    rb = [vol(6 + a) for a in range(3)]
+    where = tvf.tv_fgp_run_h(bt, p, ra, rb, 0.003, 1, 6)
+    torch.cuda.synchronize()
+    r = rb if where else ra
+    host = to_host_bits(store)
+    nan = lambda h: ((h & 0x7C00) == 0x7C00) & ((h & 0x3FF) != 0)
+    assert nan(host[:, :guard]).all() and nan(host[:, guard + n:]).all()
+    assert_bits_equal(np.stack([to_host_bits(t) for t in p]), pe, "p")
+    assert_bits_equal(np.stack([to_host_bits(t) for t in r]), re, "r")

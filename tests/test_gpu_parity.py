@@ -18,7 +18,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
-VARIANTS = ["fused", "lds_march", "two_kernel", "point", "reg_march"]
+VARIANTS = ["fused", "lds_march", "two_kernel", "point", "reg_march", "pair"]
 
 
 @pytest.fixture(scope="module")
@@ -109,7 +109,8 @@ def test_workload1_blobs_128_full_200_steps(tvf, variant):
 
 RAGGED = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70),
           (65, 5, 17), (63, 3, 2), (1000, 7, 3), (2, 2, 2), (64, 4, 16), (64, 4, 17),
-          (200, 9, 33), (3, 300, 5), (1100, 10, 6), (64, 70, 10), (2100, 20, 5)]
+          (200, 9, 33), (3, 300, 5), (1100, 10, 6), (64, 70, 10), (2100, 20, 5),
+          (258, 17, 6), (126, 9, 4), (2, 1, 3)]
 
 
 @pytest.mark.parametrize("dims", RAGGED, ids=lambda d: "x".join(map(str, d)))
@@ -138,8 +139,8 @@ def test_r_different_from_p(tvf, variant):
     assert_bitwise(got, exp, "r != p " + variant)
 
 
-def test_single_step_with_explicit_momentum(tvf):
-    dims = (77, 19, 11)
+@pytest.mark.parametrize("dims", [(77, 19, 11), (78, 19, 11)], ids=["nx77", "nx78"])
+def test_single_step_with_explicit_momentum(tvf, dims):
     b, p0, r0 = phantoms.make_inputs(4, dims)
     m = np.float32(0.61803)
     pe, re = oracle.step(b, p0, r0, 0.003, m)
@@ -209,13 +210,15 @@ def test_non_default_stream(tvf):
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
-def test_nan_guard_bands(tvf, variant):
+@pytest.mark.parametrize("dims,guard", [((67, 9, 18), 4096), ((130, 9, 18), 4096),
+                                        ((130, 9, 18), 4097)],
+                         ids=["nx67", "nx130", "nx130_odd_offset"])
+def test_nan_guard_bands(tvf, variant, dims, guard):
     """Buffers sit between NaN guard bands: no write may touch them, no read
-    of them may reach a result."""
-    dims = (67, 9, 18)
+    of them may reach a result.  An odd guard length leaves the volumes
+    aligned to one element but not two."""
     nx, ny, nz = dims
     n = nx * ny * nz
-    guard = 4096
     b, p0, r0 = phantoms.make_inputs(4, dims)
     exp = oracle_solve(b, p0, r0, 0.003, 1, 6)
     dev = torch.device("cuda")
@@ -263,9 +266,11 @@ def test_workload2_256_variants_agree(tvf):
 def test_workload3_512_full_200_steps(tvf):
     """The headline volume: all 134M voxels after the full 20 x 10 steps."""
     b, p0, r0, lam, no, ni, exp = reference(3)
-    got = gpu_solve(tvf, b, p0, r0, lam, no, ni, "fused")
-    assert_close(got, exp, "ellipsoids 512^3")
-    assert_bitwise(got, exp, "ellipsoids 512^3")
+    for variant in ("fused", "pair"):
+        got = gpu_solve(tvf, b, p0, r0, lam, no, ni, variant)
+        assert_close(got, exp, "ellipsoids 512^3 " + variant)
+        assert_bitwise(got, exp, "ellipsoids 512^3 " + variant)
+        del got
     _cache.clear()
 
 

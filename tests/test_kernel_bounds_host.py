@@ -21,9 +21,13 @@ CSRC = os.path.join(ROOT, "stencil_dual_update_amd", "csrc")
 
 SHAPES = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70), (65, 5, 17),
           (63, 3, 2), (2, 2, 2), (64, 8, 4), (64, 8, 5), (64, 4, 16), (128, 16, 8),
-          (1100, 10, 7), (2100, 20, 5), (3, 300, 5), (200, 9, 33)]
-VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "reg_march", "point",
-            "two_kernel", "lds_march", "primal", "primal_h", "gap"]
+          (1100, 10, 7), (2100, 20, 5), (3, 300, 5), (200, 9, 33), (2, 1, 1), (258, 17, 6),
+          (126, 9, 4)]
+VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
+            "pair_h", "pair_nostream_h", "reg_march", "point", "two_kernel", "lds_march", "primal",
+            "primal_h", "gap"]
+FOUR_PLANE = ("fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
+              "pair_h", "pair_nostream_h", "point", "gap")
 
 
 def compiler():
@@ -49,9 +53,7 @@ def test_every_access_in_bounds(emul, variant):
         for wide in (0, 1):
             for end in (0, 1):
                 for grid in ((0, 7) if wide else (0,)):
-                    for planes in ((8, 3) if variant not in ("fused", "fused_nostream", "fused_h",
-                                                             "fused_nostream_h", "point", "gap")
-                                   else (4,)):
+                    for planes in ((8, 3) if variant not in FOUR_PLANE else (4,)):
                         args = [emul, variant, str(nx), str(ny), str(nz), str(wide), str(grid),
                                 str(end), str(planes)]
                         r = subprocess.run(args, capture_output=True, text=True, timeout=120)
