@@ -44,10 +44,15 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_512.json")
 METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
 
 
+# Sources the default fp32 kernel is compiled from (its traffic record is valid
+# only while these are unchanged).
+DEFAULT_KERNEL_SOURCES = ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp", "tv_fgp_fused.hip")
+
+
 def kernel_source_digest():
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "stencil_dual_update_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in DEFAULT_KERNEL_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()

