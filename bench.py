@@ -37,8 +37,10 @@ import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
+# algorithmic bytes per voxel per launch, and FGP steps per launch
 BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "reg_march": 52, "pair": 52,
-                   "two_kernel": 72}
+                   "two_kernel": 72, "tb2": 52}
+STEPS_PER_LAUNCH = {"tb2": 2}
 BYTES_PER_VOXEL_HALF = 28
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_512.json")
 METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
@@ -176,7 +178,9 @@ def main():
         p = p.to(torch.float16)  # round to nearest even, as the oracle's half mode
     ra = p.clone()
     rb = torch.empty_like(ra)
-    ws = torch.empty_like(b) if variant == tvf.TWO_KERNEL else None
+    ws = (torch.empty_like(b) if variant == tvf.TWO_KERNEL else
+          torch.empty_like(p) if variant == tvf.TB2 else None)
+    spl = 1 if half else STEPS_PER_LAUNCH.get(args.variant, 1)
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
@@ -216,23 +220,33 @@ def main():
         wall_ms = (time.perf_counter() - t_wall) * 1e3
         region_ms = start.elapsed_time(stop)
 
-        # per-launch durations: an event pair around every launch
+        # per-launch durations: an event pair around every launch (a launch of
+        # the two-steps-per-pass kernel runs steps k and k+1, p_in -> p_out)
+        n_launch = max(1, args.steps // spl)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-               for _ in range(args.steps)]
-        for k in range(args.steps):
-            m = tvf.momentum(k % n_inner + 1)
-            evs[k][0].record(stream)
-            step(r_cur, r_nxt, m)
-            evs[k][1].record(stream)
+               for _ in range(n_launch)]
+        p_cur, p_alt = p, ws
+        for q in range(n_launch):
+            k = q * spl
+            evs[q][0].record(stream)
+            if spl == 2:
+                tvf.tv_fgp_step2(b, p_cur, p_alt, r_cur, r_nxt, lam,
+                                 tvf.momentum(k % n_inner + 1),
+                                 tvf.momentum((k + 1) % n_inner + 1), stream=stream)
+                p_cur, p_alt = p_alt, p_cur
+            else:
+                step(r_cur, r_nxt, tvf.momentum(k % n_inner + 1))
+            evs[q][1].record(stream)
             r_cur, r_nxt = r_nxt, r_cur
         torch.cuda.synchronize()
+        p = p_cur
         launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
 
     ms_per_step = region_ms / args.steps
     step_bytes = (BYTES_PER_VOXEL_HALF if half else BYTES_PER_VOXEL[args.variant]) * nvox
     launch_avg_ms = float(np.mean(launch_ms))
     achieved = step_bytes / (launch_avg_ms * 1e-3) / 1e9
-    region_gbs = step_bytes / (ms_per_step * 1e-3) / 1e9
+    region_gbs = step_bytes / spl / (ms_per_step * 1e-3) / 1e9
 
     # duality-gap reduction (reads b and p: 16 B per voxel), of the fp32 dual
     if half:
@@ -328,6 +342,7 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
                      "algorithmic_bytes_per_launch": step_bytes,
+                     "steps_per_launch": spl,
                      "launch_ms_avg": round(launch_avg_ms, 5),
                      "launch_ms_min": round(float(np.min(launch_ms)), 5),
                      "launch_ms_max": round(float(np.max(launch_ms)), 5)},

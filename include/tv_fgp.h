@@ -73,6 +73,13 @@ extern "C" {
                                 (128x8 tiles, pair loads and stores) where nx is even
                                 and every volume is aligned to two elements; the
                                 fused kernel otherwise                               */
+#define TV_FGP_TB2        6  /* two steps per pass over HBM: the first step runs on
+                                the tile grown by one voxel and stays on chip, the
+                                second is written (temporal blocking along z; 52 B
+                                per voxel per two steps).  Used by tv_fgp_run and
+                                tv_fgp_solve, which need a workspace of three
+                                volumes for the second p; a single step
+                                (tv_fgp_step_ex) runs the fused kernel            */
 
 /*
  * One FGP step ("TV solver: the FGP step on the GPU", section "What one step
@@ -99,7 +106,8 @@ int tv_fgp_step(const float *b, float *const p[3], const float *const r_in[3],
  * tv_fgp_step with an explicit variant (TV_FGP_*).  z_ws is a device buffer
  * of at least tv_fgp_workspace_bytes(variant, ...) bytes; it is required by
  * TV_FGP_TWO_KERNEL (which leaves the primal z of r in it) and ignored
- * (may be NULL) otherwise.  Same page and section as tv_fgp_step.
+ * (may be NULL) otherwise (TV_FGP_TB2 runs a single step with the fused
+ * kernel and needs none here).  Same page and section as tv_fgp_step.
  */
 int tv_fgp_step_ex(const float *b, float *const p[3],
                    const float *const r_in[3], float *const r_out[3],
@@ -116,17 +124,42 @@ int tv_fgp_step_ex(const float *b, float *const p[3],
  * for the k-th step of each outer iteration (m_1 = 0).  p and r carry over
  * between outer iterations.
  *   r_a, r_b  [in/out]  the two momentum buffers; the first step reads r_a.
- *                       After every step the roles swap.
+ *                       After every step the roles swap (with TV_FGP_TB2,
+ *                       after every launch, which may run two steps).
  *   r_final   [out]     host pointer, may be NULL; receives 0 if the last
  *                       momentum copy is in r_a, 1 if in r_b.
  * With n_outer * n_inner == 0 nothing is enqueued and *r_final = 0.
  * Other arguments as tv_fgp_step_ex.  p, r_a, r_b and z_ws must not overlap
  * each other or b.
+ * TV_FGP_TB2: z_ws holds three volumes (tv_fgp_workspace_bytes), used as a
+ * second p buffer: the steps of each outer iteration run in pairs, one
+ * launch per pair, p alternating between the caller's p and z_ws; an odd
+ * last step runs the fused kernel in place; if p ends in z_ws it is copied
+ * back into p on the stream.  Results equal those of the other variants bit
+ * for bit; only the buffer named by r_final may differ.
  */
 int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
                float *const r_b[3], float lambda, int n_outer, int n_inner,
                int64_t nx, int64_t ny, int64_t nz, int variant, float *z_ws,
                void *stream, int *r_final);
+
+/*
+ * Two consecutive FGP steps ("TV solver: the FGP step on the GPU", section
+ * "What one step does", applied twice) in one pass over the volumes: the
+ * first with momentum m1, the second with m2.  Reads b, p_in and r_in once,
+ * writes p_out and r_out once (52 bytes per voxel for two steps).  The result
+ * is bit for bit that of tv_fgp_step(m1) followed by tv_fgp_step(m2), with p
+ * ending in p_out and the second step's momentum copy in r_out.
+ *   p_in  [in]   the dual before the first step (not modified)
+ *   p_out [out]  the dual after the second step
+ * p_in must be a separate buffer from p_out: the pass reads p_in around each
+ * tile while neighbouring tiles write p_out.  No written buffer (p_out,
+ * r_out) may overlap any other buffer.  Status codes as tv_fgp_step; m1 and
+ * m2 must be finite.
+ */
+int tv_fgp_step2(const float *b, const float *const p_in[3], float *const p_out[3],
+                 const float *const r_in[3], float *const r_out[3], float lambda,
+                 float m1, float m2, int64_t nx, int64_t ny, int64_t nz, void *stream);
 
 /*
  * Primal read-out z = max(b - lambda * L(p), 0) from a dual field p, with the
@@ -220,9 +253,10 @@ int tv_fgp_solve(const float *b, float *const p[3], float *const r_a[3],
                  double gap_host[3]);
 
 /*
- * Bytes of z workspace `variant` needs at these dimensions: nx*ny*nz*4 for
- * TV_FGP_TWO_KERNEL, 0 for the others.  Returns 0 for invalid dimensions or
- * an unknown variant.
+ * Bytes of workspace a run of `variant` needs at these dimensions:
+ * nx*ny*nz*4 for TV_FGP_TWO_KERNEL (z), 3*nx*ny*nz*4 for TV_FGP_TB2 (a
+ * second p, three consecutive volumes), 0 for the others.  Returns 0 for
+ * invalid dimensions or an unknown variant.
  */
 size_t tv_fgp_workspace_bytes(int variant, int64_t nx, int64_t ny, int64_t nz);
 

@@ -27,11 +27,13 @@ TWO_KERNEL = 2
 POINT = 3
 REG_MARCH = 4
 PAIR = 5
+TB2 = 6
 VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
-            "point": POINT, "reg_march": REG_MARCH, "pair": PAIR}
+            "point": POINT, "reg_march": REG_MARCH, "pair": PAIR,
+            "tb2": TB2}
 
 # Names declared in include/tv_fgp.h, in declaration order.
-EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_primal",
+EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_fgp_step2", "tv_primal",
            "tv_fgp_step_h", "tv_fgp_run_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
            "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_status_string",
            "tv_fgp_variant_name")
@@ -70,6 +72,8 @@ def _load():
     lib.tv_fgp_run.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int,
                                I64, I64, I64, ctypes.c_int, P, P,
                                ctypes.POINTER(ctypes.c_int)]
+    lib.tv_fgp_step2.restype = ctypes.c_int
+    lib.tv_fgp_step2.argtypes = [P, P3, P3, P3, P3, F, F, F, I64, I64, I64, P]
     lib.tv_primal.restype = ctypes.c_int
     lib.tv_primal.argtypes = [P, P3, P, F, I64, I64, I64, P]
     lib.tv_fgp_step_h.restype = ctypes.c_int
@@ -163,6 +167,14 @@ def _check_volume(t, shape, what):
         raise ValueError("%s has shape %s, expected %s" % (what, tuple(t.shape), shape))
 
 
+def _check_ws(t, shape, variant, what="z_ws"):
+    """The run workspace: one volume, or three (a (3, nz, ny, nx) tensor) for TB2."""
+    if variant == TB2 and t is not None and not isinstance(t, int):
+        _check_volume(t, (3,) + shape, what)
+    else:
+        _check_volume(t, shape, what)
+
+
 def _check_half(t, shape, what):
     if t is None or isinstance(t, int):
         return
@@ -247,7 +259,7 @@ def tv_fgp_run(b, p, r_a, r_b, lam, n_outer, n_inner, variant=FUSED, z_ws=None,
     nx, ny, nz = _dims_of(b, dims)
     shape = (nz, ny, nx)
     _check_volume(b, shape, "b")
-    _check_volume(z_ws, shape, "z_ws")
+    _check_ws(z_ws, shape, variant)
     where = ctypes.c_int(-1)
     st = lib.tv_fgp_run(_addr(b), _field(p, shape, "p"), _field(r_a, shape, "r_a"),
                         _field(r_b, shape, "r_b"), float(lam), int(n_outer),
@@ -255,6 +267,17 @@ def tv_fgp_run(b, p, r_a, r_b, lam, n_outer, n_inner, variant=FUSED, z_ws=None,
                         _stream(stream), ctypes.byref(where))
     _raise(st, "tv_fgp_run")
     return where.value
+
+
+def tv_fgp_step2(b, p_in, p_out, r_in, r_out, lam, m1, m2, stream=None, dims=None):
+    """Two FGP steps (momentum m1, then m2) in one pass: p_in -> p_out, r_in -> r_out."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    st = lib.tv_fgp_step2(_addr(b), _field(p_in, shape, "p_in"), _field(p_out, shape, "p_out"),
+                          _field(r_in, shape, "r_in"), _field(r_out, shape, "r_out"),
+                          float(lam), float(m1), float(m2), nx, ny, nz, _stream(stream))
+    _raise(st, "tv_fgp_step2")
 
 
 def tv_primal(b, p, z, lam, stream=None, dims=None):
@@ -304,7 +327,7 @@ def tv_fgp_solve(b, p, r_a, r_b, lam, max_outer, n_inner, tol, gap_ws, gap_dev,
     nx, ny, nz = _dims_of(b, dims)
     shape = (nz, ny, nx)
     _check_volume(b, shape, "b")
-    _check_volume(z_ws, shape, "z_ws")
+    _check_ws(z_ws, shape, variant)
     ws_bytes = gap_workspace_bytes(nx, ny, nz)
     _check_dev(gap_ws, "gap_ws", "float64", ws_bytes // 8)
     _check_dev(gap_dev, "gap_dev", "float64", 3)

@@ -93,12 +93,80 @@ tvfgp::StepArgs make_step(const float *b, float *const p[3],
 
 int launch_status(int rc) { return rc == 0 ? TV_OK : TV_ERR_LAUNCH; }
 
+// Inner loop of the two-steps-per-pass variant: steps are launched in pairs
+// (one pass each, p alternating between the caller's p and the workspace
+// p_ws), an odd last step of an outer iteration runs the fused kernel in
+// place, and if p ends in the workspace it is copied back.
+int enqueue_steps_tb2(const float *b, float *const p[3], float *const r_a[3],
+                      float *const r_b[3], float lambda, float c, int n_outer,
+                      int n_inner, int64_t nx, int64_t ny, int64_t nz,
+                      float *p_ws, size_t bytes, void *stream, int *where) {
+  const size_t n = bytes / sizeof(float);
+  float *const ws[3] = {p_ws, p_ws + n, p_ws + 2 * n};
+  float *const *cur = p;
+  float *const *alt = ws;
+  for (int o = 0; o < n_outer; ++o) {
+    double t = 1.0;
+    for (int k = 1; k <= n_inner;) {
+      const int todo = n_inner - k + 1 >= 2 ? 2 : 1;
+      float m[2];
+      // m_k and m_{k+1}, evaluated as in the one-step loop
+      for (int s = 0; s < todo; ++s) {
+        const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
+        m[s] = (float)((t - 1.0) / t_next);
+        t = t_next;
+      }
+      float *const *in = *where ? r_b : r_a;
+      float *const *out = *where ? r_a : r_b;
+      if (todo == 2) {
+        tvfgp::Step2Args a;
+        a.b = b;
+        for (int q = 0; q < 3; ++q) {
+          a.p_in[q] = cur[q];
+          a.p_out[q] = alt[q];
+          a.r_in[q] = in[q];
+          a.r_out[q] = out[q];
+        }
+        a.lam = lambda;
+        a.c = c;
+        a.m1 = m[0];
+        a.m2 = m[1];
+        a.nx = nx;
+        a.ny = ny;
+        a.nz = nz;
+        a.stream = stream;
+        if (tvfgp::launch_tb2(a) != 0) return TV_ERR_LAUNCH;
+        float *const *tmp = cur;
+        cur = alt;
+        alt = tmp;
+      } else {
+        const float *cin[3] = {in[0], in[1], in[2]};
+        if (tvfgp::launch_step(make_step(b, cur, cin, out, lambda, c, m[0], nx, ny, nz,
+                                         tvfgp::kVariantFused, nullptr, stream)) != 0)
+          return TV_ERR_LAUNCH;
+      }
+      *where ^= 1;
+      k += todo;
+    }
+  }
+  if (cur != p) {
+    for (int q = 0; q < 3; ++q)
+      if (hipMemcpyAsync(p[q], cur[q], bytes, hipMemcpyDeviceToDevice,
+                         (hipStream_t)stream) != hipSuccess)
+        return TV_ERR_LAUNCH;
+  }
+  return TV_OK;
+}
+
 // Enqueue n_outer x n_inner steps; `where` (0: r_a holds r, 1: r_b) is
 // updated after every step, so the caller learns where the last r is.
 int enqueue_steps(const float *b, float *const p[3], float *const r_a[3],
                   float *const r_b[3], float lambda, float c, int n_outer,
                   int n_inner, int64_t nx, int64_t ny, int64_t nz, int variant,
                   float *z_ws, void *stream, int *where) {
+  if (variant == tvfgp::kVariantTb2)
+    return enqueue_steps_tb2(b, p, r_a, r_b, lambda, c, n_outer, n_inner, nx, ny, nz, z_ws,
+                             volume_bytes(nx, ny, nz), stream, where);
   for (int o = 0; o < n_outer; ++o) {
     double t = 1.0;
     for (int k = 1; k <= n_inner; ++k) {
@@ -116,6 +184,14 @@ int enqueue_steps(const float *b, float *const p[3], float *const r_a[3],
     }
   }
   return TV_OK;
+}
+
+// Workspace a run of `variant` needs for volumes of `bytes`: the two-kernel
+// variant's z, the two-steps-per-pass variant's second p (three volumes).
+size_t run_workspace_bytes(int variant, size_t bytes) {
+  if (variant == tvfgp::kVariantTwoKernel) return bytes;
+  if (variant == tvfgp::kVariantTb2) return 3 * bytes;
+  return 0;
 }
 
 size_t gap_ws_bytes(int64_t nx, int64_t ny, int64_t nz) {
@@ -183,16 +259,16 @@ static int check_run(const float *b, float *const p[3], float *const r_a[3],
   if (bytes == 0) return TV_ERR_DIMS;
   int st = check_lambda(lambda, c_out);
   if (st != TV_OK) return st;
-  const bool two = variant == tvfgp::kVariantTwoKernel;
-  if (two && z_ws == nullptr) return TV_ERR_WORKSPACE;
+  const size_t ws = run_workspace_bytes(variant, bytes);
+  if (ws != 0 && z_ws == nullptr) return TV_ERR_WORKSPACE;
   const Buf bufs[11] = {vol(b, bytes, false),     vol(p[0], bytes, true),
                         vol(p[1], bytes, true),   vol(p[2], bytes, true),
                         vol(r_a[0], bytes, true), vol(r_a[1], bytes, true),
                         vol(r_a[2], bytes, true), vol(r_b[0], bytes, true),
                         vol(r_b[1], bytes, true), vol(r_b[2], bytes, true),
-                        vol(z_ws, bytes, true)};
+                        vol(z_ws, ws, true)};
   *bytes_out = bytes;
-  return check_buffers(bufs, two ? 11 : 10);
+  return check_buffers(bufs, ws != 0 ? 11 : 10);
 }
 
 int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
@@ -210,6 +286,45 @@ int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
                      variant, z_ws, stream, &where);
   if (r_final) *r_final = where;
   return st;
+}
+
+int tv_fgp_step2(const float *b, const float *const p_in[3], float *const p_out[3],
+                 const float *const r_in[3], float *const r_out[3], float lambda,
+                 float m1, float m2, int64_t nx, int64_t ny, int64_t nz, void *stream) {
+  if (p_in == nullptr || p_out == nullptr || r_in == nullptr || r_out == nullptr)
+    return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  if (!isfinite(m1) || !isfinite(m2)) return TV_ERR_PARAM;
+  const Buf bufs[13] = {vol(b, bytes, false),        vol(p_in[0], bytes, false),
+                        vol(p_in[1], bytes, false),  vol(p_in[2], bytes, false),
+                        vol(p_out[0], bytes, true),  vol(p_out[1], bytes, true),
+                        vol(p_out[2], bytes, true),  vol(r_in[0], bytes, false),
+                        vol(r_in[1], bytes, false),  vol(r_in[2], bytes, false),
+                        vol(r_out[0], bytes, true),  vol(r_out[1], bytes, true),
+                        vol(r_out[2], bytes, true)};
+  st = check_buffers(bufs, 13);
+  if (st != TV_OK) return st;
+  tvfgp::Step2Args a;
+  a.b = b;
+  for (int q = 0; q < 3; ++q) {
+    a.p_in[q] = p_in[q];
+    a.p_out[q] = p_out[q];
+    a.r_in[q] = r_in[q];
+    a.r_out[q] = r_out[q];
+  }
+  a.lam = lambda;
+  a.c = c;
+  a.m1 = m1;
+  a.m2 = m2;
+  a.nx = nx;
+  a.ny = ny;
+  a.nz = nz;
+  a.stream = stream;
+  return launch_status(tvfgp::launch_tb2(a));
 }
 
 int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
@@ -425,7 +540,8 @@ int tv_fgp_solve(const float *b, float *const p[3], float *const r_a[3],
     extra[n_extra++] = vol(r_a[k], bytes, true);
     extra[n_extra++] = vol(r_b[k], bytes, true);
   }
-  if (variant == tvfgp::kVariantTwoKernel) extra[n_extra++] = vol(z_ws, bytes, true);
+  const size_t ws = run_workspace_bytes(variant, bytes);
+  if (ws != 0) extra[n_extra++] = vol(z_ws, ws, true);
   st = check_gap(b, p, lambda, nx, ny, nz, gap_dev, gap_ws, gap_ws_bytes_given,
                  extra, n_extra);
   if (st != TV_OK) return st;
@@ -463,8 +579,7 @@ int tv_fgp_solve(const float *b, float *const p[3], float *const r_a[3],
 
 size_t tv_fgp_workspace_bytes(int variant, int64_t nx, int64_t ny, int64_t nz) {
   if (!known_variant(variant)) return 0;
-  if (variant != tvfgp::kVariantTwoKernel) return 0;
-  return volume_bytes(nx, ny, nz);
+  return run_workspace_bytes(variant, volume_bytes(nx, ny, nz));
 }
 
 const char *tv_fgp_status_string(int status) {
@@ -490,6 +605,7 @@ const char *tv_fgp_variant_name(int variant) {
     case tvfgp::kVariantPoint: return "point";
     case tvfgp::kVariantRegMarch: return "reg_march";
     case tvfgp::kVariantPair: return "pair";
+    case tvfgp::kVariantTb2: return "tb2";
     default: return nullptr;
   }
 }

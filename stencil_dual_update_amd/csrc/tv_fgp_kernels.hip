@@ -47,6 +47,8 @@ int launch_step_t(const StepArgs &a) {
       return launch_lds_march(a);
     case kVariantPair:
       return launch_fused_pair(a);
+    case kVariantTb2:  // a single step: the fused kernel
+      return launch_fused_zx(a);
     default:
       return kLaunchFailed;
   }

@@ -14,7 +14,8 @@ constexpr int kVariantTwoKernel = 2;
 constexpr int kVariantPoint = 3;
 constexpr int kVariantRegMarch = 4;
 constexpr int kVariantPair = 5;
-constexpr int kNumVariants = 6;
+constexpr int kVariantTb2 = 6;
+constexpr int kNumVariants = 7;
 
 constexpr int kLaunchFailed = -1;
 
@@ -35,6 +36,19 @@ struct StepArgs {
   int64_t planes;    // planes per tile along z
   int variant;
   void *stream;      // hipStream_t
+};
+
+// Two consecutive steps in one pass (momentum m1, then m2): p is read from
+// p_in and written to p_out, r from r_in to r_out.
+struct Step2Args {
+  const float *b;
+  const float *p_in[3];
+  float *p_out[3];
+  const float *r_in[3];
+  float *r_out[3];
+  float lam, c, m1, m2;
+  int64_t nx, ny, nz;
+  void *stream;
 };
 
 struct PrimalArgs {
@@ -89,6 +103,7 @@ int launch_fused_zx_h(const StepArgsH &a);
 // elements; otherwise the one-voxel kernel above.
 int launch_fused_pair(const StepArgs &a);
 int launch_fused_pair_h(const StepArgsH &a);
+int launch_tb2(const Step2Args &a);
 int launch_primal_h(const PrimalArgsH &a);
 // Duality gap of p (two kernels: partial sums, then their fixed-order sum).
 int launch_duality_gap(const GapArgs &a);

@@ -11,7 +11,7 @@
 // usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
 //   variant: fused | fused_nostream | fused_h | fused_nostream_h | pair | pair_nostream |
 //            pair_h | pair_nostream_h | reg_march | point | two_kernel | lds_march |
-//            primal | primal_h | gap
+//            primal | primal_h | gap | tb2
 //   (the pair variants need an even nx; with an odd one they report "ok" without running)
 //   wide: 1 instantiates the 64-bit offset / index path regardless of size
 #include <stdio.h>
@@ -25,6 +25,7 @@
 #include "tv_fgp_gap_kernel.hpp"
 #include "tv_fgp_lds_kernel.hpp"
 #include "tv_fgp_pair_kernel.hpp"
+#include "tv_fgp_tb2_kernel.hpp"
 
 thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
 
@@ -75,8 +76,18 @@ unsigned pick_grid(int64_t ntiles, unsigned override_grid) {
 }
 
 struct Bufs {
-  float *b, *p[3], *ri[3], *ro[3], *z;
+  float *b, *p[3], *ri[3], *ro[3], *z, *po[3];
 };
+
+template <typename I, typename Off>
+void run_tb2(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid) {
+  const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz);
+  run_grid(pick_grid(g.ntiles, grid), tvfgp::kTbBlock, [&] {
+    tvfgp::tb2_kernel<I, Off>(v.b, v.p[0], v.p[1], v.p[2], v.po[0], v.po[1], v.po[2], v.ri[0],
+                              v.ri[1], v.ri[2], v.ro[0], v.ro[1], v.ro[2], 0.01f, 8.3f, 0.3f,
+                              0.5f, g);
+  });
+}
 
 template <typename I, typename Off, typename S>
 void run_pair(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid,
@@ -203,12 +214,18 @@ int main(int argc, char **argv) {
     v.ro[a] = guarded(dbytes, end_aligned, seed++);
   }
   v.z = guarded(bytes, end_aligned, seed++);
+  for (int a = 0; a < 3; ++a) v.po[a] = guarded(dbytes, end_aligned, seed++);
   if (!strcmp(variant, "fused") || !strcmp(variant, "fused_nostream")) {
     const bool sp = !strcmp(variant, "fused");
     if (wide)
       run_fused<int64_t, uint64_t, float>(v, nx, ny, nz, grid, sp);
     else
       run_fused<int32_t, uint32_t, float>(v, nx, ny, nz, grid, sp);
+  } else if (!strcmp(variant, "tb2")) {
+    if (wide)
+      run_tb2<int64_t, uint64_t>(v, nx, ny, nz, grid);
+    else
+      run_tb2<int32_t, uint32_t>(v, nx, ny, nz, grid);
   } else if (!strncmp(variant, "pair", 4)) {
     const bool sp = strstr(variant, "nostream") == nullptr;
     if (nx % 2 != 0) {

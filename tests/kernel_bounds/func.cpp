@@ -1,0 +1,154 @@
+// CPU functional emulation of the HIP kernels (test infrastructure).
+//
+// The kernel headers are compiled as host C++ with the shim in threaded mode:
+// every thread of a workgroup runs as an OS thread and __syncthreads() is a
+// real barrier over them, so data exchanged through LDS (a static array here,
+// shared by the workgroup's threads; workgroups run one after another) behaves
+// as on the GPU.  Arithmetic is IEEE binary32 with no contraction, as on the
+// GPU, so results can be compared bit for bit with the CPU oracle.
+//
+// usage: func <kernel> <nx> <ny> <nz> <lambda> <m1> <m2> <dir> <wide:0|1> <grid:0=as launched>
+//   kernel: fused  one step (m1), p updated in place
+//           tb2    two steps (m1 then m2) in one pass, p_in -> p_out
+//   dir holds b.bin (n floats), p.bin and r.bin (3n floats each); the kernel
+//   writes p_out.bin and r_out.bin there.
+#include <condition_variable>
+#include <mutex>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "tv_fgp_fused_kernel.hpp"
+#include "tv_fgp_tb2_kernel.hpp"
+
+thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
+
+namespace {
+
+struct Barrier {
+  std::mutex mu;
+  std::condition_variable cv;
+  unsigned count = 0, waiting = 0, generation = 0;
+  void wait() {
+    std::unique_lock<std::mutex> lock(mu);
+    const unsigned gen = generation;
+    if (++waiting == count) {
+      waiting = 0;
+      ++generation;
+      cv.notify_all();
+    } else {
+      cv.wait(lock, [&] { return gen != generation; });
+    }
+  }
+};
+
+Barrier g_barrier;
+
+}  // namespace
+
+void emul_syncthreads() { g_barrier.wait(); }
+
+namespace {
+
+template <typename F>
+void run_grid(unsigned grid, unsigned block, F &&body) {
+  g_barrier.count = block;
+  for (unsigned bl = 0; bl < grid; ++bl) {
+    std::vector<std::thread> threads;
+    threads.reserve(block);
+    for (unsigned th = 0; th < block; ++th) {
+      threads.emplace_back([&, bl, th] {
+        gridDim = {grid, 1, 1};
+        blockDim = {block, 1, 1};
+        blockIdx = {bl, 0, 0};
+        threadIdx = {th, 0, 0};
+        body();
+      });
+    }
+    for (auto &t : threads) t.join();
+  }
+}
+
+std::vector<float> read_file(const std::string &path, size_t n) {
+  std::vector<float> v(n);
+  FILE *f = fopen(path.c_str(), "rb");
+  if (!f || fread(v.data(), sizeof(float), n, f) != n) {
+    fprintf(stderr, "cannot read %s\n", path.c_str());
+    exit(3);
+  }
+  fclose(f);
+  return v;
+}
+
+void write_file(const std::string &path, const std::vector<float> &v) {
+  FILE *f = fopen(path.c_str(), "wb");
+  if (!f || fwrite(v.data(), sizeof(float), v.size(), f) != v.size()) {
+    fprintf(stderr, "cannot write %s\n", path.c_str());
+    exit(3);
+  }
+  fclose(f);
+}
+
+unsigned pick(int64_t ntiles, unsigned grid) {
+  return grid ? grid : tvfgp::grid_for(ntiles);
+}
+
+template <typename I, typename Off>
+void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, float m1, float m2,
+         unsigned grid, const float *b, float *p, float *r, float *p_out, float *r_out) {
+  const size_t n = (size_t)(nx * ny * nz);
+  const float c = 1.0f / (12.0f * lam);
+  if (!strcmp(kernel, "fused")) {
+    const auto g = tvfgp::zx_geometry<I, Off>(nx, ny, nz);
+    run_grid(pick(g.ntiles, grid), tvfgp::kZxBlock, [&] {
+      tvfgp::fused_zx_kernel<I, Off, true, float>(b, p, p + n, p + 2 * n, r, r + n, r + 2 * n,
+                                                  r_out, r_out + n, r_out + 2 * n, lam, c, m1,
+                                                  g);
+    });
+    memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "tb2")) {
+    const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz);
+    run_grid(pick(g.ntiles, grid), tvfgp::kTbBlock, [&] {
+      tvfgp::tb2_kernel<I, Off>(b, p, p + n, p + 2 * n, p_out, p_out + n, p_out + 2 * n, r,
+                                r + n, r + 2 * n, r_out, r_out + n, r_out + 2 * n, lam, c, m1,
+                                m2, g);
+    });
+  } else {
+    fprintf(stderr, "unknown kernel %s\n", kernel);
+    exit(2);
+  }
+}
+
+}  // namespace
+
+int main(int argc, char **argv) {
+  if (argc != 11) {
+    fprintf(stderr, "usage: func kernel nx ny nz lambda m1 m2 dir wide grid\n");
+    return 2;
+  }
+  const char *kernel = argv[1];
+  const int64_t nx = atoll(argv[2]), ny = atoll(argv[3]), nz = atoll(argv[4]);
+  const float lam = strtof(argv[5], nullptr), m1 = strtof(argv[6], nullptr),
+              m2 = strtof(argv[7], nullptr);
+  const std::string dir = argv[8];
+  const bool wide = atoi(argv[9]) != 0;
+  const unsigned grid = (unsigned)atoi(argv[10]);
+  const size_t n = (size_t)(nx * ny * nz);
+  std::vector<float> b = read_file(dir + "/b.bin", n);
+  std::vector<float> p = read_file(dir + "/p.bin", 3 * n);
+  std::vector<float> r = read_file(dir + "/r.bin", 3 * n);
+  std::vector<float> p_out(3 * n, -12345.0f), r_out(3 * n, -12345.0f);
+  if (wide)
+    run<int64_t, uint64_t>(kernel, nx, ny, nz, lam, m1, m2, grid, b.data(), p.data(),
+                           r.data(), p_out.data(), r_out.data());
+  else
+    run<int32_t, uint32_t>(kernel, nx, ny, nz, lam, m1, m2, grid, b.data(), p.data(),
+                           r.data(), p_out.data(), r_out.data());
+  write_file(dir + "/p_out.bin", p_out);
+  write_file(dir + "/r_out.bin", r_out);
+  printf("ok %s %lldx%lldx%lld\n", kernel, (long long)nx, (long long)ny, (long long)nz);
+  return 0;
+}

@@ -19,7 +19,14 @@ struct EmulDim3 {
 
 extern thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
 
-// Threads run one after another, so a barrier has nothing to wait for; LDS
-// contents are then meaningless, but every address a thread forms is the
-// one it forms on the GPU, which is what the check is about.
+#ifdef TVFGP_EMUL_THREADS
+// Functional emulation: every thread of a workgroup is an OS thread and the
+// barrier is a real one (func.cpp), so LDS exchanges behave as on the GPU.
+void emul_syncthreads();
+inline void __syncthreads() { emul_syncthreads(); }
+#else
+// Bounds check: threads run one after another, so a barrier has nothing to
+// wait for; LDS contents are then meaningless, but every address a thread
+// forms is the one it forms on the GPU, which is what the check is about.
 inline void __syncthreads() {}
+#endif

@@ -89,6 +89,8 @@ def test_workspace_bytes():
     for v in (tvf.FUSED, tvf.LDS_MARCH, tvf.POINT, tvf.REG_MARCH):
         assert tvf.workspace_bytes(v, 10, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.TWO_KERNEL, 0, 20, 30) == 0
+    assert tvf.workspace_bytes(tvf.TB2, 10, 20, 30) == 3 * 10 * 20 * 30 * 4
+    assert tvf.workspace_bytes(tvf.PAIR, 10, 20, 30) == 0
     assert tvf.workspace_bytes(7, 10, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.TWO_KERNEL, 1 << 31, 1 << 31, 1 << 31) == 0
 
@@ -117,7 +119,7 @@ def test_workspace_bytes():
     (dict(lam=1e-45), tvf.TV_ERR_PARAM),           # 1/(12 lambda) overflows
     (dict(m=float("nan")), tvf.TV_ERR_PARAM),
     (dict(m=float("inf")), tvf.TV_ERR_PARAM),
-    (dict(variant=6), tvf.TV_ERR_VARIANT),
+    (dict(variant=7), tvf.TV_ERR_VARIANT),
     (dict(variant=-1), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),       # two-kernel without z
     (dict(variant=2, ws=0), tvf.TV_ERR_ALIAS),     # workspace aliases b
@@ -167,8 +169,10 @@ def run(b=0, p=(1, 2, 3), ra=(4, 5, 6), rb=(7, 8, 9), lam=0.01, n_outer=2, n_inn
     (dict(rb=(7, 8, 4)), tvf.TV_ERR_ALIAS),        # r_b aliases r_a
     (dict(ra=(4, 5, 1)), tvf.TV_ERR_ALIAS),        # r_a aliases p
     (dict(dims=(NX, NY, -4)), tvf.TV_ERR_DIMS),
-    (dict(variant=6), tvf.TV_ERR_VARIANT),
+    (dict(variant=7), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),
+    (dict(variant=6), tvf.TV_ERR_WORKSPACE),       # two steps per pass without p workspace
+    (dict(variant=6, ws=9), tvf.TV_ERR_ALIAS),     # first workspace volume is r_b[2]
 ])
 def test_run_rejects(kw, code):
     st, where = run(**kw)
@@ -307,3 +311,41 @@ def test_primal_h_rejects():
         == tvf.TV_ERR_ALIAS
     assert L.tv_primal_h(addr(0), field(1, 2, 3), None, 0.01, NX, NY, NZ, None) \
         == tvf.TV_ERR_NULL
+
+
+def test_run_tb2_accepts_three_volume_workspace():
+    # nothing is enqueued with n_outer = 0, so the checks alone decide
+    st, where = run(variant=tvf.TB2, ws=10, n_outer=0)
+    assert st == tvf.TV_OK and where == 0
+
+
+def test_run_tb2_workspace_spans_three_volumes():
+    # b placed inside the third volume of the workspace overlaps it; just past it, not
+    ws = addr(10)
+    for b_addr, code in ((ws + 2 * VOL + 4, tvf.TV_ERR_ALIAS), (ws + 3 * VOL, tvf.TV_OK)):
+        where = ctypes.c_int(-7)
+        st = L.tv_fgp_run(b_addr, field(1, 2, 3), field(4, 5, 6), field(7, 8, 9), 0.01, 0, 3,
+                          NX, NY, NZ, tvf.TB2, ws, None, ctypes.byref(where))
+        assert st == code
+
+
+def step2(b=0, pi=(1, 2, 3), po=(10, 11, 12), ri=(4, 5, 6), ro=(7, 8, 9), lam=0.01, m1=0.0,
+          m2=0.3, dims=(NX, NY, NZ)):
+    return L.tv_fgp_step2(None if b is None else addr(b), field(*pi), field(*po), field(*ri),
+                          field(*ro), lam, m1, m2, *dims, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=None), tvf.TV_ERR_NULL),
+    (dict(po=(10, None, 12)), tvf.TV_ERR_NULL),
+    (dict(dims=(NX, 0, NZ)), tvf.TV_ERR_DIMS),
+    (dict(lam=-1.0), tvf.TV_ERR_PARAM),
+    (dict(m1=float("nan")), tvf.TV_ERR_PARAM),
+    (dict(m2=float("inf")), tvf.TV_ERR_PARAM),
+    (dict(po=(1, 11, 12)), tvf.TV_ERR_ALIAS),   # p_out on p_in: the pass needs both
+    (dict(po=(10, 11, 4)), tvf.TV_ERR_ALIAS),   # p_out on r_in
+    (dict(ro=(7, 8, 0)), tvf.TV_ERR_ALIAS),     # r_out on b
+    (dict(ro=(7, 8, 12)), tvf.TV_ERR_ALIAS),    # r_out on p_out
+])
+def test_step2_rejects(kw, code):
+    assert step2(**kw) == code

@@ -29,7 +29,7 @@ def test_volume_past_2_31_voxels_all_variants():
     n = nx * ny * nz
     assert n > 2 ** 31
     free, _ = torch.cuda.mem_get_info()
-    need = 12 * n * 4
+    need = 14 * n * 4
     assert free > need, "needs %.0f GB of device memory, %.0f GB free" % (need / 1e9, free / 1e9)
     b = phantoms.make_uniform(DIMS, seed=11, lo=-0.01, hi=0.05)
     dev = torch.device("cuda")
@@ -37,7 +37,8 @@ def test_volume_past_2_31_voxels_all_variants():
     p = torch.empty((3, nz, ny, nx), device=dev)
     ra = torch.empty_like(p)
     rb = torch.empty_like(p)
-    ws = torch.empty_like(bt)
+    ws3 = torch.empty_like(p)  # second p of the two-steps-per-pass variant
+    ws = ws3[0]                 # z of the two-kernel variant, then the read-out
     pts = [(0, 0, 0), (nz - 1, ny - 1, nx - 1), (nz // 2, ny // 2, nx // 2), (7, 1299, 0),
            (1199, 0, 1399), (600, 8 * 81, 64 * 16), (601, 8 * 81 - 1, 64 * 16 - 1),
            (1100, 517, 1023), (3, 4, 1024), (1196, 1297, 700)]
@@ -54,7 +55,8 @@ def test_volume_past_2_31_voxels_all_variants():
         p.zero_()
         ra.zero_()
         where = tvf.tv_fgp_run(bt, p, ra, rb, LAM, 1, 2, variant=v,
-                               z_ws=ws if v == tvf.TWO_KERNEL else None)
+                               z_ws=ws if v == tvf.TWO_KERNEL else
+                               ws3 if v == tvf.TB2 else None)
         r = rb if where else ra
         tvf.tv_primal(bt, p, ws, LAM)
         torch.cuda.synchronize()
@@ -65,5 +67,5 @@ def test_volume_past_2_31_voxels_all_variants():
             assert np.array_equal(gp.view(np.uint32), pe.view(np.uint32)), (variant, c, gp, pe)
             assert np.array_equal(gr.view(np.uint32), re.view(np.uint32)), (variant, c, gr, re)
             assert np.float32(gz) == ze, (variant, c, gz, ze)
-    del bt, p, ra, rb, ws
+    del bt, p, ra, rb, ws, ws3
     torch.cuda.empty_cache()

@@ -18,7 +18,16 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
-VARIANTS = ["fused", "lds_march", "two_kernel", "point", "reg_march", "pair"]
+VARIANTS = ["fused", "lds_march", "two_kernel", "point", "reg_march", "pair", "tb2"]
+
+
+def run_workspace(tvf, v, like):
+    """The workspace a run of variant v needs: z (two-kernel) or a second p (tb2)."""
+    if v == tvf.TWO_KERNEL:
+        return torch.empty_like(like)
+    if v == tvf.TB2:
+        return torch.empty((3,) + tuple(like.shape), dtype=like.dtype, device=like.device)
+    return None
 
 
 @pytest.fixture(scope="module")
@@ -36,7 +45,7 @@ def gpu_solve(tvf, b, p0, r0, lam, n_outer, n_inner, variant="fused", stream=Non
     p = torch.from_numpy(np.ascontiguousarray(p0)).to(dev)
     ra = torch.from_numpy(np.ascontiguousarray(r0)).to(dev)
     rb = torch.full_like(ra, float("nan"))
-    ws = torch.empty_like(bt) if v == tvf.TWO_KERNEL else None
+    ws = run_workspace(tvf, v, bt)
     where = tvf.tv_fgp_run(bt, p, ra, rb, lam, n_outer, n_inner, variant=v, z_ws=ws,
                            stream=stream)
     r = rb if where else ra
@@ -151,13 +160,40 @@ def test_single_step_with_explicit_momentum(tvf, dims):
         p = torch.from_numpy(p0).to(dev)
         ri = torch.from_numpy(r0).to(dev)
         ro = torch.empty_like(ri)
-        ws = torch.empty_like(bt) if v == tvf.TWO_KERNEL else None
+        ws = run_workspace(tvf, v, bt) if v == tvf.TWO_KERNEL else None
         tvf.tv_fgp_step(bt, p, ri, ro, 0.003, float(m), variant=v, z_ws=ws)
         torch.cuda.synchronize()
         got = (p.cpu().numpy(), ro.cpu().numpy(), oracle.primal(b, p.cpu().numpy(), 0.003))
         exp = (pe, re, oracle.primal(b, pe, 0.003))
         assert_bitwise(got, exp, "single step " + variant)
         assert np.array_equal(ri.cpu().numpy(), r0), "r_in was modified"
+
+
+STEP2_DIMS = [(67, 45, 29), (130, 17, 33), (64, 8, 16), (64, 8, 17), (1, 1, 1), (5, 70, 3),
+              (1, 1, 40), (200, 3, 2), (129, 9, 47)]
+
+
+@pytest.mark.parametrize("dims", STEP2_DIMS, ids=lambda d: "x".join(map(str, d)))
+def test_step2_equals_two_oracle_steps(tvf, dims):
+    """One two-steps-per-pass launch against two oracle steps, from a state with r != p."""
+    b, p0, _ = phantoms.make_inputs(4, dims)
+    rng = np.random.default_rng(17)
+    r0 = (p0 + 0.3 * rng.standard_normal(p0.shape)).astype(np.float32)
+    m1, m2 = np.float32(0.3), np.float32(0.61)
+    pe, re = oracle.step(b, p0, r0, 0.003, m1)
+    pe, re = oracle.step(b, pe, re, 0.003, m2)
+    dev = torch.device("cuda")
+    bt = torch.from_numpy(b).to(dev)
+    pi = torch.from_numpy(p0).to(dev)
+    ri = torch.from_numpy(r0).to(dev)
+    po = torch.full_like(pi, float("nan"))
+    ro = torch.full_like(ri, float("nan"))
+    tvf.tv_fgp_step2(bt, pi, po, ri, ro, 0.003, float(m1), float(m2))
+    torch.cuda.synchronize()
+    got_p = po.cpu().numpy()
+    assert_bitwise((got_p, ro.cpu().numpy(), oracle.primal(b, got_p, 0.003)),
+                   (pe, re, oracle.primal(b, pe, 0.003)), "step2 %s" % (dims,))
+    assert np.array_equal(pi.cpu().numpy(), p0) and np.array_equal(ri.cpu().numpy(), r0)
 
 
 # --------------------------------------------------------------------------
@@ -236,6 +272,10 @@ def test_nan_guard_bands(tvf, variant, dims, guard):
     ra = [vol(4 + a, r0[a]) for a in range(3)]
     rb = [vol(7 + a) for a in range(3)]
     ws = vol(10) if v == tvf.TWO_KERNEL else None
+    ws_store = None
+    if v == tvf.TB2:  # three consecutive volumes between guard bands
+        ws_store = torch.full((3 * n + 2 * guard,), float("nan"), device=dev)
+        ws = ws_store[guard:guard + 3 * n].view(3, nz, ny, nx)
     where = tvf.tv_fgp_run(bt, p, ra, rb, 0.003, 1, 6, variant=v, z_ws=ws)
     torch.cuda.synchronize()
     r = rb if where else ra
@@ -243,6 +283,9 @@ def test_nan_guard_bands(tvf, variant, dims, guard):
     got_r = np.stack([t.cpu().numpy() for t in r])
     host = store.cpu().numpy()
     assert np.isnan(host[:, :guard]).all() and np.isnan(host[:, guard + n:]).all()
+    if ws_store is not None:
+        wh = ws_store.cpu().numpy()
+        assert np.isnan(wh[:guard]).all() and np.isnan(wh[guard + 3 * n:]).all()
     assert_bitwise((got_p, got_r, oracle.primal(b, got_p, 0.003)), exp, "guard " + variant)
 
 
@@ -266,7 +309,7 @@ def test_workload2_256_variants_agree(tvf):
 def test_workload3_512_full_200_steps(tvf):
     """The headline volume: all 134M voxels after the full 20 x 10 steps."""
     b, p0, r0, lam, no, ni, exp = reference(3)
-    for variant in ("fused", "pair"):
+    for variant in ("fused", "pair", "tb2"):
         got = gpu_solve(tvf, b, p0, r0, lam, no, ni, variant)
         assert_close(got, exp, "ellipsoids 512^3 " + variant)
         assert_bitwise(got, exp, "ellipsoids 512^3 " + variant)

@@ -22,11 +22,11 @@ CSRC = os.path.join(ROOT, "stencil_dual_update_amd", "csrc")
 SHAPES = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70), (65, 5, 17),
           (63, 3, 2), (2, 2, 2), (64, 8, 4), (64, 8, 5), (64, 4, 16), (128, 16, 8),
           (1100, 10, 7), (2100, 20, 5), (3, 300, 5), (200, 9, 33), (2, 1, 1), (258, 17, 6),
-          (126, 9, 4)]
+          (126, 9, 4), (66, 10, 40), (130, 17, 33)]
 VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
             "pair_h", "pair_nostream_h", "reg_march", "point", "two_kernel", "lds_march", "primal",
-            "primal_h", "gap"]
-FOUR_PLANE = ("fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
+            "primal_h", "gap", "tb2"]
+FOUR_PLANE = ("tb2", "fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
               "pair_h", "pair_nostream_h", "point", "gap")
 
 

@@ -1,0 +1,94 @@
+"""CPU functional emulation of kernels that exchange data through LDS (no GPU).
+
+tests/kernel_bounds/func.cpp compiles the kernel headers as host C++ with every
+thread of a workgroup as an OS thread and a real barrier for __syncthreads(),
+so the LDS rings and the barrier schedule are exercised as on the GPU.  The
+arithmetic is IEEE binary32 without contraction on both sides, so the
+emulated kernels must match the CPU oracle bit for bit.  This checks the
+two-steps-per-pass kernel's pipeline (halo regions, ring slots, slab ends)
+before any GPU run; the GPU parity tests then check the compiled code.
+"""
+import os
+import shutil
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle
+import phantoms
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+SRC = os.path.join(HERE, "kernel_bounds")
+CSRC = os.path.join(ROOT, "stencil_dual_update_amd", "csrc")
+
+
+def compiler():
+    for c in ("/opt/rocm/llvm/bin/clang++", shutil.which("clang++")):
+        if c and os.path.exists(c):
+            return c
+    pytest.skip("no clang++ (the kernels use clang vector extensions)")
+
+
+@pytest.fixture(scope="module")
+def func(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("kernel_func") / "func")
+    cmd = [compiler(), "-std=c++17", "-O1", "-ffp-contract=off", "-pthread",
+           "-DTVFGP_EMUL_THREADS", "-I", os.path.join(SRC, "shim"), "-I", CSRC, "-I",
+           os.path.join(ROOT, "include"), os.path.join(SRC, "func.cpp"), "-o", out]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return out
+
+
+def emulate(func, tmp_path, kernel, b, p0, r0, lam, m1, m2, wide=0, grid=0):
+    nz, ny, nx = b.shape
+    d = str(tmp_path)
+    b.tofile(os.path.join(d, "b.bin"))
+    p0.tofile(os.path.join(d, "p.bin"))
+    r0.tofile(os.path.join(d, "r.bin"))
+    r = subprocess.run([func, kernel, str(nx), str(ny), str(nz), repr(lam), repr(float(m1)),
+                        repr(float(m2)), d, str(wide), str(grid)],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stderr
+    pg = np.fromfile(os.path.join(d, "p_out.bin"), np.float32).reshape(p0.shape)
+    rg = np.fromfile(os.path.join(d, "r_out.bin"), np.float32).reshape(p0.shape)
+    return pg, rg
+
+
+def inputs(dims, seed=7):
+    b, p0, _ = phantoms.make_inputs(4, dims)
+    rng = np.random.default_rng(seed)
+    r0 = (p0 + 0.3 * rng.standard_normal(p0.shape)).astype(np.float32)
+    return b, p0, r0
+
+
+def assert_bits(got, exp, label):
+    bad = np.count_nonzero(got.view(np.uint32) != exp.view(np.uint32))
+    assert bad == 0, "%s: %d values differ" % (label, bad)
+
+
+def test_fused_one_step(func, tmp_path):
+    """The emulator itself: the default kernel's single step equals the oracle's."""
+    b, p0, r0 = inputs((67, 19, 11))
+    pg, rg = emulate(func, tmp_path, "fused", b, p0, r0, 0.003, np.float32(0.4), 0.0)
+    pe, re = oracle.step(b, p0, r0, 0.003, np.float32(0.4))
+    assert_bits(pg, pe, "p")
+    assert_bits(rg, re, "r")
+
+
+# (dims, 64-bit path, forced grid): slab ends, ragged x/y tails, nz below one
+# slab, one voxel, tiles looped over by a short grid
+CASES = [((65, 9, 17), 0, 0), ((64, 8, 48), 1, 0), ((130, 17, 33), 0, 3), ((1, 1, 40), 0, 0),
+         ((5, 70, 3), 0, 0), ((63, 7, 15), 0, 0), ((1, 1, 1), 0, 0), ((66, 10, 18), 1, 2)]
+
+
+@pytest.mark.parametrize("dims,wide,grid", CASES, ids=lambda c: str(c))
+def test_two_steps_per_pass(func, tmp_path, dims, wide, grid):
+    b, p0, r0 = inputs(dims)
+    m1, m2 = np.float32(0.3), np.float32(0.61)
+    pg, rg = emulate(func, tmp_path, "tb2", b, p0, r0, 0.003, m1, m2, wide, grid)
+    pe, re = oracle.step(b, p0, r0, 0.003, m1)
+    pe, re = oracle.step(b, pe, re, 0.003, m2)
+    assert_bits(pg, pe, "p %s" % (dims,))
+    assert_bits(rg, re, "r %s" % (dims,))
