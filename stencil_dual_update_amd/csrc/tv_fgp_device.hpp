@@ -75,6 +75,7 @@ __device__ __forceinline__ float primal_z(float bj, float rx, float rx_lo,
 //   g_a = z(i) - z(i+e_a), 0 at the upper a-face (has_a false)
 //   q_a = r_a(i) + c * g_a,  c = 1/(12 lambda)
 //   p'  = q / max(1, |q|),   |q| = sqrt((q_x^2 + q_y^2) + q_z^2)
+//         (IEEE square root and divisions, skipped where they cannot matter)
 //   r_out = p' + m (p' - p);  p <- p'
 // p0..p2 hold p(i) on entry and p' on return.
 __device__ __forceinline__ void dual_update(float zi, float zx, float zy,
@@ -90,11 +91,18 @@ __device__ __forceinline__ void dual_update(float zi, float zx, float zy,
   const float qy = r1 + c * gy;
   const float qz = r2 + c * gz;
   const float s2 = (qx * qx + qy * qy) + qz * qz;
-  const float nq = __builtin_sqrtf(s2);
-  const float s = nq > 1.0f ? nq : 1.0f;
-  const float px = qx / s;
-  const float py = qy / s;
-  const float pz = qz / s;
+  // s = max(1, |q|) and p' = q / s.  The rounded square root exceeds 1 exactly
+  // when s2 > 1 + 2^-23 (sqrt(1 + 2^-23) rounds to 1), so below that s = 1 and
+  // p' = q / 1 = q: the square root and the three divisions are skipped, and
+  // a wave whose lanes all stay inside the ball skips them entirely.  NaN
+  // takes the s = 1 branch, as max(1, NaN) does.
+  float px = qx, py = qy, pz = qz;
+  if (s2 > 0x1.000002p+0f) {
+    const float nq = __builtin_sqrtf(s2);
+    px = qx / nq;
+    py = qy / nq;
+    pz = qz / nq;
+  }
   o0 = px + m * (px - p0);
   o1 = py + m * (py - p1);
   o2 = pz + m * (pz - p2);

@@ -98,8 +98,10 @@ __device__ __forceinline__ void tb_init_point(TbPoint<Off> &pt, int lx, int ly, 
   pt.e1 = lx >= -1 && lx <= kTbTileX && ly >= -1 && ly <= kTbTileY;
   pt.r1 = lx >= 0 && lx <= kTbTileX && ly >= 0 && ly <= kTbTileY;
   pt.own = lx >= 0 && lx < kTbTileX && ly >= 0 && ly < kTbTileY;
-  pt.low_x = gx > 0;
-  pt.low_y = gy > 0;
+  // lower-neighbour flags only on points inside the volume, so that a load
+  // at a point outside (clamped to the column offset 0) stays in bounds
+  pt.low_x = pt.ok && gx > 0;
+  pt.low_y = pt.ok && gy > 0;
   pt.has_x = gx + 1 < g.nx;
   pt.has_y = gy + 1 < g.ny;
   pt.o = pt.ok ? ((Off)gx + (Off)g.nx * (Off)gy) * (Off)4 : (Off)0;
@@ -111,6 +113,8 @@ __device__ __forceinline__ void tb_init_point(TbPoint<Off> &pt, int lx, int ly, 
 }
 
 // Loads of plane kp into the "next" registers (caller checks 0 <= kp < nz).
+// A point outside the volume has offset 0 and loads the plane's first voxel,
+// which is in bounds; its values are never used.
 template <typename Off>
 __device__ __forceinline__ void tb_load(TbPoint<Off> &pt, Off kp_off, Off sy4,
                                         const float *__restrict__ b,
@@ -152,8 +156,11 @@ __device__ __forceinline__ void tb_rotate(TbPoint<Off> &pt) {
   pt.c1l = pt.n1l;
 }
 
+// Six waves per SIMD (three workgroups per CU) measured ~9% faster than the
+// five the unconstrained register allocation allows; the cap costs a couple
+// of spilled registers.
 template <typename I, typename Off>
-__global__ __launch_bounds__(kTbBlock) void tb2_kernel(
+__global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
     const float *__restrict__ b, const float *__restrict__ pi0,
     const float *__restrict__ pi1, const float *__restrict__ pi2,
     float *__restrict__ po0, float *__restrict__ po1, float *__restrict__ po2,
@@ -194,12 +201,12 @@ __global__ __launch_bounds__(kTbBlock) void tb2_kernel(
     // and the inputs of plane z0 - 1 as "current"
     if (z0 - 2 >= 0) {
       const Off j = (Off)(z0 - 2) * sz4;
-      if (own.ok) own.q2 = ld(ri2, own.o + j);
-      if (hal.ok) hal.q2 = ld(ri2, hal.o + j);
+      own.q2 = ld(ri2, own.o + j);
+      if (has_halo) hal.q2 = ld(ri2, hal.o + j);
     }
     if (input_plane(z0 - 1)) {
-      if (own.ok) tb_load(own, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
-      if (hal.ok) tb_load(hal, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
+      tb_load(own, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
+      if (has_halo) tb_load(hal, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
     }
     tb_take(own);
     tb_take(hal);
@@ -215,12 +222,10 @@ __global__ __launch_bounds__(kTbBlock) void tb2_kernel(
       // p_in of the step-one plane
       if (do_d) {
         const Off j = (Off)kd * sz4;
-        if (own.ok) {
-          own.pp0 = ld(pi0, own.o + j);
-          own.pp1 = ld(pi1, own.o + j);
-          own.pp2 = ld(pi2, own.o + j);
-        }
-        if (hal.ok && hal.e1) {
+        own.pp0 = ld(pi0, own.o + j);
+        own.pp1 = ld(pi1, own.o + j);
+        own.pp2 = ld(pi2, own.o + j);
+        if (has_halo) {
           hal.pp0 = ld(pi0, hal.o + j);
           hal.pp1 = ld(pi1, hal.o + j);
           hal.pp2 = ld(pi2, hal.o + j);
@@ -229,18 +234,21 @@ __global__ __launch_bounds__(kTbBlock) void tb2_kernel(
       // inputs of plane k+4, consumed next iteration
       const I kl = k + 4;
       if (input_plane(kl)) {
-        if (own.ok) tb_load(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
-        if (hal.ok) tb_load(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+        tb_load(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+        if (has_halo) tb_load(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
       }
 
       // ---- phase 1: z1 of plane k+1 on R1, z0 of plane k+3 on R0
       auto phase_f = [&](TbPoint<Off> &pt) {
         const int x = pt.lx + 1, y = pt.ly + 1;
         const int s = (int)(kf & 1), sp = (int)((kf + 1) & 1);
+        // every index is inside the arrays (x, y >= 1 on R1), so all reads
+        // are unconditional and the boundary rule is a select
         const float rx = rxs[y][x], ry = rys[y][x], rz = rzs[s][y][x];
-        const float rxl = pt.low_x ? rxs[y][x - 1] : 0.0f;
-        const float ryl = pt.low_y ? rys[y - 1][x] : 0.0f;
-        const float rzl = kf > 0 ? rzs[sp][y][x] : 0.0f;
+        const float rxm = rxs[y][x - 1], rym = rys[y - 1][x], rzm = rzs[sp][y][x];
+        const float rxl = pt.low_x ? rxm : 0.0f;
+        const float ryl = pt.low_y ? rym : 0.0f;
+        const float rzl = kf > 0 ? rzm : 0.0f;
         z1r[s][pt.ly][pt.lx] = primal_z(pt.bqq, rx, rxl, ry, ryl, rz, rzl, lam);
       };
       auto phase_b = [&](TbPoint<Off> &pt) {
