@@ -1,21 +1,26 @@
 """Benchmark of the FGP step on one MI355X.
 
-Prints one JSON line.  A "step" is one FGP step over the whole volume (one
-launch of the fused kernel); the default workload is the 512^3 ellipsoid
-phantom, 20 outer x 10 inner steps, lambda = 0.002.  The timed region runs
-exactly --steps steps (in outer iterations of 10, momentum restarted at each)
-on one stream, bracketed by device synchronisation; inputs are resident in
-HBM before it starts.
+Prints one JSON line.  The metric is ms per FGP step over the whole volume;
+the default workload is the 512^3 ellipsoid phantom, 20 outer x 10 inner
+steps, lambda = 0.002, run by tv_fgp_run with the two-steps-per-pass kernel
+(variant tb2: steps k and k+1 of an outer iteration in one launch, bit for
+bit the same as two one-step launches).  The timed region runs exactly
+--steps steps (in outer iterations of 10, momentum restarted at each) on one
+stream, bracketed by device synchronisation; inputs are resident in HBM
+before it starts.
 
 Besides the headline ms/step it reports:
   roofline      algorithmic bytes per launch (52 B per voxel: read b, r (3),
-                p (3); write p (3), r (3)) over the average launch duration,
-                timed with events around every launch on the launch stream,
-                against MI355X's 8 TB/s HBM peak; `traffic` is the HBM bytes
-                per launch from the rocprofv3 FETCH_SIZE / WRITE_SIZE record
-                committed under profiles/ (null when the kernel sources have
-                changed since those counters were taken); `bench.py --traffic`
-                builds that record from the two counter runs
+                p (3); write p (3), r (3); for tb2 that covers two steps) over
+                the average launch duration, timed with events around every
+                launch on the launch stream, against MI355X's 8 TB/s HBM peak;
+                `traffic` is the HBM bytes per launch from the rocprofv3
+                FETCH_SIZE / WRITE_SIZE record committed under profiles/
+                (null when the kernel's sources have changed since those
+                counters were taken); `bench.py --traffic` builds that record
+                from the two counter runs
+  one_step_kernel  the one-step fused kernel (tv_fgp_step's default) timed
+                launch by launch on the same data, with its own traffic record
   gap_kernel    time of one duality-gap evaluation of the final p (reads b and
                 p: 16 B per voxel) and the gap triple itself
   copy          bandwidth of a plain device copy of 2 x 1 GiB on the same box
@@ -24,7 +29,7 @@ Besides the headline ms/step it reports:
                 the same workload at full size (with --storage half: the first
                 outer iteration, 10 steps, of the oracle's half mode)
 
---storage half runs the same step with p and r stored as binary16 (fp32
+--storage half runs the step with p and r stored as binary16 (fp32
 arithmetic; 28 B per voxel: read b, r (3), p (3) at 4 + 6 + 6 B, write p (3),
 r (3) at 6 + 6 B); its CPU baseline is the oracle's half mode.
 """
@@ -42,19 +47,27 @@ BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "reg_march": 52, "
                    "two_kernel": 72, "tb2": 52}
 STEPS_PER_LAUNCH = {"tb2": 2}
 BYTES_PER_VOXEL_HALF = 28
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_fused_512.json")
 METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
 
+# Kernel measured for each variant's roofline, and the sources it is compiled
+# from: a committed traffic record (profiles/traffic_<variant>_512.json) is
+# reported only while these sources are unchanged.
+KERNELS = {
+    "tb2": ("tb2_kernel", ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp",
+                           "tv_fgp_tb2_kernel.hpp", "tv_fgp_tb2.hip")),
+    "fused": ("fused_zx_kernel", ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp",
+                                  "tv_fgp_fused.hip")),
+}
 
-# Sources the default fp32 kernel is compiled from (its traffic record is valid
-# only while these are unchanged).
-DEFAULT_KERNEL_SOURCES = ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp", "tv_fgp_fused.hip")
+
+def traffic_file(variant):
+    return os.path.join(ROOT, "profiles", "traffic_%s_512.json" % variant)
 
 
-def kernel_source_digest():
+def kernel_source_digest(variant):
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "stencil_dual_update_amd", "csrc")
-    for name in DEFAULT_KERNEL_SOURCES:
+    for name in KERNELS[variant][1]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()
@@ -62,11 +75,12 @@ def kernel_source_digest():
 
 def measured_traffic(variant, workload):
     """HBM bytes per launch from the committed counter summary, if current."""
-    if variant != "fused" or workload != 3 or not os.path.exists(TRAFFIC_FILE):
+    path = traffic_file(variant)
+    if variant not in KERNELS or workload != 3 or not os.path.exists(path):
         return None
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         rec = json.load(f)
-    if rec.get("kernel_source_sha256") != kernel_source_digest():
+    if rec.get("kernel_source_sha256") != kernel_source_digest(variant):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -82,38 +96,40 @@ def _counter_rows(path):
     return list(rows.values())
 
 
-def write_traffic(fetch_csv, write_csv, out=TRAFFIC_FILE):
+def write_traffic(fetch_csv, write_csv, variant):
     """Turn two rocprofv3 --pmc runs of this bench (FETCH_SIZE, then WRITE_SIZE,
-    KiB per dispatch) into the per-launch HBM traffic of the fused kernel.
+    KiB per dispatch) into the per-launch HBM traffic of the variant's kernel.
 
     Each counter is scaled by what it reads for the bench's copy probe, a
     device copy of exactly 1 GiB read + 1 GiB written.
     """
     import statistics
+    kname = KERNELS[variant][0]
     res = {}
     for key, path in (("fetch", fetch_csv), ("write", write_csv)):
         rows = _counter_rows(path)
         copy = [r["value"] for r in rows if "copyBuffer" in r["name"]]
-        fused = [r["value"] for r in rows if "fused_zx_kernel" in r["name"]]
-        if not copy or not fused:
-            raise SystemExit("%s: no copy or fused dispatches found" % path)
+        kern = [r["value"] for r in rows if kname in r["name"]]
+        if not copy or not kern:
+            raise SystemExit("%s: no copy or %s dispatches found" % (path, kname))
         copy_kib = statistics.median(copy)
         scale = (1 << 20) / copy_kib          # KiB of 1 GiB / counter reading
-        res[key] = {"kernel_kib_median": statistics.median(fused),
+        res[key] = {"kernel_kib_median": statistics.median(kern),
                     "copy_kib_median": copy_kib, "scale": scale,
-                    "dispatches": len(fused)}
+                    "dispatches": len(kern)}
     fetch_b = res["fetch"]["kernel_kib_median"] * res["fetch"]["scale"] * 1024
     write_b = res["write"]["kernel_kib_median"] * res["write"]["scale"] * 1024
     vol = 512 ** 3 * 4
-    rec = {"kernel": "fused_zx_kernel", "workload": "ellipsoids 512^3",
-           "kernel_source_sha256": kernel_source_digest(),
+    rec = {"kernel": kname, "variant": variant, "workload": "ellipsoids 512^3",
+           "steps_per_launch": STEPS_PER_LAUNCH.get(variant, 1),
+           "kernel_source_sha256": kernel_source_digest(variant),
            "fetch": res["fetch"], "write": res["write"],
            "hbm_read_bytes_per_launch": round(fetch_b),
            "hbm_write_bytes_per_launch": round(write_b),
            "hbm_bytes_per_launch": round(fetch_b + write_b),
            "volumes_read": round(fetch_b / vol, 3), "volumes_written": round(write_b / vol, 3),
-           "algorithmic_bytes_per_launch": 52 * 512 ** 3}
-    with open(out, "w") as f:
+           "algorithmic_bytes_per_launch": BYTES_PER_VOXEL[variant] * 512 ** 3}
+    with open(traffic_file(variant), "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
 
@@ -126,8 +142,9 @@ def parse():
     ap.add_argument("--workload", type=int, default=3, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--dims", type=int, nargs=3, metavar=("NX", "NY", "NZ"),
                     help="run the workload's recipe at other dimensions")
-    ap.add_argument("--variant", default="fused",
-                    choices=sorted(BYTES_PER_VOXEL))
+    ap.add_argument("--variant", default=None, choices=sorted(BYTES_PER_VOXEL),
+                    help="kernel variant (default: tb2, two steps per pass; fused with "
+                         "--storage half)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg")
     ap.add_argument("--storage", default="f32", choices=["f32", "half"],
@@ -141,8 +158,10 @@ def parse():
 
 def main():
     args = parse()
+    if args.variant is None:
+        args.variant = "fused" if args.storage == "half" else "tb2"
     if args.traffic:
-        write_traffic(*args.traffic)
+        write_traffic(*args.traffic, args.variant)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -248,6 +267,27 @@ def main():
     achieved = step_bytes / (launch_avg_ms * 1e-3) / 1e9
     region_gbs = step_bytes / spl / (ms_per_step * 1e-3) / 1e9
 
+    # the one-step kernel (tv_fgp_step's default) timed alongside, launch by launch
+    one_step = None
+    if spl > 1:
+        with torch.cuda.stream(stream):
+            n1 = 50
+            ev1 = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(n1 + 5)]
+            for q in range(n1 + 5):
+                ev1[q][0].record(stream)
+                tvf.tv_fgp_step(b, p, r_cur, r_nxt, lam, tvf.momentum(q % n_inner + 1),
+                                stream=stream)
+                ev1[q][1].record(stream)
+                r_cur, r_nxt = r_nxt, r_cur
+            torch.cuda.synchronize()
+        ms1 = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev1[5:]]))
+        gbs1 = 52 * nvox / (ms1 * 1e-3) / 1e9
+        one_step = {"kernel": "fused_zx_kernel", "ms_per_step": round(ms1, 5),
+                    "achieved_gbps": round(gbs1, 1), "frac": round(gbs1 / HBM_PEAK_GBS, 4),
+                    "traffic": None if args.dims else measured_traffic("fused", args.workload),
+                    "launches": n1}
+
     # duality-gap reduction (reads b and p: 16 B per voxel), of the fp32 dual
     if half:
         p = p.float()
@@ -346,6 +386,7 @@ def main():
                      "launch_ms_avg": round(launch_avg_ms, 5),
                      "launch_ms_min": round(float(np.min(launch_ms)), 5),
                      "launch_ms_max": round(float(np.max(launch_ms)), 5)},
+        "one_step_kernel": one_step,
         "gap_kernel": gap,
         "copy": copy,
         "pct_of_copy": (round(100.0 * region_gbs / copy["gbps"], 1) if copy else None),

@@ -50,7 +50,7 @@ namespace tvfgp {
 constexpr int kTbTileX = 64;
 constexpr int kTbTileY = 8;
 constexpr int kTbBlock = kTbTileX * kTbTileY;
-constexpr int kTbPlanes = 16;    // output planes per tile
+constexpr int kTbPlanes = 32;    // output planes per tile
 constexpr int kTbGroupMax = 16;  // tile columns per group in the tile order
 constexpr int kTbReach = 64;     // tiles whose reads one XCD's L2 holds
 constexpr int kTbR0X = kTbTileX + 3, kTbR0Y = kTbTileY + 3;
