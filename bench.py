@@ -44,7 +44,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 # algorithmic bytes per voxel per launch, and FGP steps per launch
 BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "reg_march": 52, "pair": 52,
-                   "two_kernel": 72, "tb2": 52}
+                   "two_kernel": 72, "tb2": 52, "cube": 52, "cube_32x8x2": 52,
+                   "cube_64x8x1": 52, "cube_8x8x8": 52, "cube_32x4x4": 52}
 STEPS_PER_LAUNCH = {"tb2": 2}
 BYTES_PER_VOXEL_HALF = 28
 METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"

@@ -80,6 +80,14 @@ extern "C" {
                                 tv_fgp_solve, which need a workspace of three
                                 volumes for the second p; a single step
                                 (tv_fgp_step_ex) runs the fused kernel            */
+#define TV_FGP_CUBE       7  /* ablation: the page's shared-memory cube tiling; a
+                                workgroup stages b and r of a 16x8x4 cube plus a
+                                one-voxel shell in LDS, computes z once for the
+                                cube and its upper faces, then updates the cube   */
+#define TV_FGP_CUBE_32x8x2 8 /* the same with 32x8x2 cubes (tile-shape sweep)    */
+#define TV_FGP_CUBE_64x8x1 9 /* ... 64x8x1 (one plane per cube)                   */
+#define TV_FGP_CUBE_8x8x8 10 /* ... 8x8x8                                         */
+#define TV_FGP_CUBE_32x4x4 11 /* ... 32x4x4                                       */
 
 /*
  * One FGP step ("TV solver: the FGP step on the GPU", section "What one step

@@ -7,7 +7,7 @@ points: ``tv_fgp_step``, ``tv_fgp_run``, ``tv_primal``, ``tv_fgp_duality_gap``,
 ``tv_fgp_solve``.
 """
 from ._lib import (  # noqa: F401
-    EXPORTS, FUSED, LDS_MARCH, PAIR, POINT, REG_MARCH, TB2, TWO_KERNEL, VARIANTS, LIB_PATH,
+    EXPORTS, CUBE, FUSED, LDS_MARCH, PAIR, POINT, REG_MARCH, TB2, TWO_KERNEL, VARIANTS, LIB_PATH,
     TV_ERR_ALIAS, TV_ERR_ALIGN, TV_ERR_DIMS, TV_ERR_LAUNCH, TV_ERR_NULL,
     TV_ERR_PARAM, TV_ERR_VARIANT, TV_ERR_WORKSPACE, TV_OK, TvFgpError, lib,
     gap_workspace_bytes, momentum, status_string, tv_fgp_duality_gap, tv_fgp_run,

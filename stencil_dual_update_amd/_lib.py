@@ -28,9 +28,11 @@ POINT = 3
 REG_MARCH = 4
 PAIR = 5
 TB2 = 6
+CUBE = 7
 VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
             "point": POINT, "reg_march": REG_MARCH, "pair": PAIR,
-            "tb2": TB2}
+            "tb2": TB2, "cube": CUBE, "cube_32x8x2": 8, "cube_64x8x1": 9, "cube_8x8x8": 10,
+            "cube_32x4x4": 11}
 
 # Names declared in include/tv_fgp.h, in declaration order.
 EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_fgp_step2", "tv_primal",

@@ -606,6 +606,11 @@ const char *tv_fgp_variant_name(int variant) {
     case tvfgp::kVariantRegMarch: return "reg_march";
     case tvfgp::kVariantPair: return "pair";
     case tvfgp::kVariantTb2: return "tb2";
+    case tvfgp::kVariantCube: return "cube";
+    case tvfgp::kVariantCube32x8x2: return "cube_32x8x2";
+    case tvfgp::kVariantCube64x8x1: return "cube_64x8x1";
+    case tvfgp::kVariantCube8x8x8: return "cube_8x8x8";
+    case tvfgp::kVariantCube32x4x4: return "cube_32x4x4";
     default: return nullptr;
   }
 }

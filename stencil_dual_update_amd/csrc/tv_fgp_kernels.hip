@@ -49,6 +49,12 @@ int launch_step_t(const StepArgs &a) {
       return launch_fused_pair(a);
     case kVariantTb2:  // a single step: the fused kernel
       return launch_fused_zx(a);
+    case kVariantCube:
+    case kVariantCube32x8x2:
+    case kVariantCube64x8x1:
+    case kVariantCube8x8x8:
+    case kVariantCube32x4x4:
+      return launch_cube(a);
     default:
       return kLaunchFailed;
   }

@@ -15,7 +15,12 @@ constexpr int kVariantPoint = 3;
 constexpr int kVariantRegMarch = 4;
 constexpr int kVariantPair = 5;
 constexpr int kVariantTb2 = 6;
-constexpr int kNumVariants = 7;
+constexpr int kVariantCube = 7;  // 16 x 8 x 4 cubes, then other cube shapes
+constexpr int kVariantCube32x8x2 = 8;
+constexpr int kVariantCube64x8x1 = 9;
+constexpr int kVariantCube8x8x8 = 10;
+constexpr int kVariantCube32x4x4 = 11;
+constexpr int kNumVariants = 12;
 
 constexpr int kLaunchFailed = -1;
 
@@ -104,6 +109,8 @@ int launch_fused_zx_h(const StepArgsH &a);
 int launch_fused_pair(const StepArgs &a);
 int launch_fused_pair_h(const StepArgsH &a);
 int launch_tb2(const Step2Args &a);
+// Cube-tiled ablation, shape chosen by a.variant (kVariantCube...).
+int launch_cube(const StepArgs &a);
 int launch_primal_h(const PrimalArgsH &a);
 // Duality gap of p (two kernels: partial sums, then their fixed-order sum).
 int launch_duality_gap(const GapArgs &a);

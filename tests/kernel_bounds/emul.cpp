@@ -11,7 +11,8 @@
 // usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
 //   variant: fused | fused_nostream | fused_h | fused_nostream_h | pair | pair_nostream |
 //            pair_h | pair_nostream_h | reg_march | point | two_kernel | lds_march |
-//            primal | primal_h | gap | tb2
+//            primal | primal_h | gap | tb2 | cube | cube_32x8x2 | cube_64x8x1 |
+//            cube_8x8x8 | cube_32x4x4
 //   (the pair variants need an even nx; with an odd one they report "ok" without running)
 //   wide: 1 instantiates the 64-bit offset / index path regardless of size
 #include <stdio.h>
@@ -26,6 +27,7 @@
 #include "tv_fgp_lds_kernel.hpp"
 #include "tv_fgp_pair_kernel.hpp"
 #include "tv_fgp_tb2_kernel.hpp"
+#include "tv_fgp_cube_kernel.hpp"
 
 thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
 
@@ -135,11 +137,30 @@ void run_fused(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid,
     });
 }
 
+template <typename I, int TX, int TY, int TZ>
+void run_cube(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid) {
+  const auto g = tvfgp::cube_geometry<I, TX, TY, TZ>(nx, ny, nz);
+  run_grid(pick_grid(g.ntiles, grid), tvfgp::kCubeBlock, [&] {
+    tvfgp::cube_kernel<I, TX, TY, TZ>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2],
+                                      v.ro[0], v.ro[1], v.ro[2], 0.01f, 8.3f, 0.5f, g);
+  });
+}
+
 template <typename I>
 void run_ablation(const char *variant, const Bufs &v, int64_t nx, int64_t ny, int64_t nz,
                   unsigned grid, int64_t planes) {
   using namespace tvfgp;
-  if (!strcmp(variant, "reg_march")) {
+  if (!strcmp(variant, "cube")) {
+    run_cube<I, 16, 8, 4>(v, nx, ny, nz, grid);
+  } else if (!strcmp(variant, "cube_32x8x2")) {
+    run_cube<I, 32, 8, 2>(v, nx, ny, nz, grid);
+  } else if (!strcmp(variant, "cube_64x8x1")) {
+    run_cube<I, 64, 8, 1>(v, nx, ny, nz, grid);
+  } else if (!strcmp(variant, "cube_8x8x8")) {
+    run_cube<I, 8, 8, 8>(v, nx, ny, nz, grid);
+  } else if (!strcmp(variant, "cube_32x4x4")) {
+    run_cube<I, 32, 4, 4>(v, nx, ny, nz, grid);
+  } else if (!strcmp(variant, "reg_march")) {
     const Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
     run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
       fused_march_kernel<I>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2],

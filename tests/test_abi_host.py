@@ -81,7 +81,7 @@ def test_status_strings_distinct():
 def test_variant_names():
     for name, v in tvf.VARIANTS.items():
         assert tvf.variant_name(v) == name
-    assert tvf.variant_name(9) is None
+    assert tvf.variant_name(12) is None
 
 
 def test_workspace_bytes():
@@ -91,7 +91,8 @@ def test_workspace_bytes():
     assert tvf.workspace_bytes(tvf.TWO_KERNEL, 0, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.TB2, 10, 20, 30) == 3 * 10 * 20 * 30 * 4
     assert tvf.workspace_bytes(tvf.PAIR, 10, 20, 30) == 0
-    assert tvf.workspace_bytes(7, 10, 20, 30) == 0
+    assert tvf.workspace_bytes(12, 10, 20, 30) == 0
+    assert tvf.workspace_bytes(tvf.CUBE, 10, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.TWO_KERNEL, 1 << 31, 1 << 31, 1 << 31) == 0
 
 
@@ -119,7 +120,7 @@ def test_workspace_bytes():
     (dict(lam=1e-45), tvf.TV_ERR_PARAM),           # 1/(12 lambda) overflows
     (dict(m=float("nan")), tvf.TV_ERR_PARAM),
     (dict(m=float("inf")), tvf.TV_ERR_PARAM),
-    (dict(variant=7), tvf.TV_ERR_VARIANT),
+    (dict(variant=12), tvf.TV_ERR_VARIANT),
     (dict(variant=-1), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),       # two-kernel without z
     (dict(variant=2, ws=0), tvf.TV_ERR_ALIAS),     # workspace aliases b
@@ -169,7 +170,7 @@ def run(b=0, p=(1, 2, 3), ra=(4, 5, 6), rb=(7, 8, 9), lam=0.01, n_outer=2, n_inn
     (dict(rb=(7, 8, 4)), tvf.TV_ERR_ALIAS),        # r_b aliases r_a
     (dict(ra=(4, 5, 1)), tvf.TV_ERR_ALIAS),        # r_a aliases p
     (dict(dims=(NX, NY, -4)), tvf.TV_ERR_DIMS),
-    (dict(variant=7), tvf.TV_ERR_VARIANT),
+    (dict(variant=12), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),
     (dict(variant=6), tvf.TV_ERR_WORKSPACE),       # two steps per pass without p workspace
     (dict(variant=6, ws=9), tvf.TV_ERR_ALIAS),     # first workspace volume is r_b[2]

@@ -18,7 +18,8 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
-VARIANTS = ["fused", "lds_march", "two_kernel", "point", "reg_march", "pair", "tb2"]
+VARIANTS = ["fused", "lds_march", "two_kernel", "point", "reg_march", "pair", "tb2", "cube",
+            "cube_32x8x2", "cube_64x8x1", "cube_8x8x8", "cube_32x4x4"]
 
 
 def run_workspace(tvf, v, like):
@@ -208,6 +209,27 @@ def test_zero_input_stays_zero(tvf, variant):
     p, r, z = gpu_solve(tvf, b, p0, p0, 0.01, 2, 10, variant)
     for a in (p, r, z):
         assert not a.any() and not np.signbit(a).any()
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_negative_zero_in_b(tvf, variant):
+    """b = -0 at some voxels: max(u, 0) must give +0 there, as (u > 0) ? u : +0 does
+    (a max instruction may keep the sign of -0), and everything after bit for bit."""
+    dims = (70, 9, 13)
+    b, p0, r0 = phantoms.make_inputs(4, dims)
+    b = b.copy()
+    b.reshape(-1)[::7] = np.float32(-0.0)
+    zero = np.zeros_like(p0)
+    z_exp = oracle.primal(b, zero, 0.003)
+    assert not np.signbit(z_exp[b == 0]).any()
+    exp = oracle_solve(b, zero, zero, 0.003, 1, 4)
+    got = gpu_solve(tvf, b, zero, zero, 0.003, 1, 4, variant)
+    assert_bitwise(got, exp, "-0 in b " + variant)
+    bt = torch.from_numpy(b).to("cuda")
+    z = torch.empty_like(bt)
+    tvf.tv_primal(bt, torch.from_numpy(zero).to("cuda"), z, 0.003)
+    torch.cuda.synchronize()
+    assert np.array_equal(z.cpu().numpy().view(np.uint32), z_exp.view(np.uint32))
 
 
 @pytest.mark.parametrize("c", [0.0, 0.037, -0.2])

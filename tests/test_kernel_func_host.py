@@ -77,6 +77,16 @@ def test_fused_one_step(func, tmp_path):
     assert_bits(rg, re, "r")
 
 
+@pytest.mark.parametrize("kernel", ["cube", "cube_8x8x8"])
+@pytest.mark.parametrize("dims", [(37, 19, 11), (16, 8, 4), (1, 1, 1)], ids=lambda d: str(d))
+def test_cube_one_step(func, tmp_path, kernel, dims):
+    b, p0, r0 = inputs(dims)
+    pg, rg = emulate(func, tmp_path, kernel, b, p0, r0, 0.003, np.float32(0.4), 0.0)
+    pe, re = oracle.step(b, p0, r0, 0.003, np.float32(0.4))
+    assert_bits(pg, pe, "p")
+    assert_bits(rg, re, "r")
+
+
 # (dims, 64-bit path, forced grid): slab ends, ragged x/y tails, nz below one
 # slab, one voxel, tiles looped over by a short grid
 CASES = [((65, 9, 17), 0, 0), ((64, 8, 48), 1, 0), ((130, 17, 33), 0, 3), ((1, 1, 40), 0, 0),
