@@ -1,15 +1,17 @@
 // LDS z-marching ablation of the FGP step for gfx950.
 //
 // The page "TV solver: the FGP step on the GPU" (table "Variants", and
-// "What made the difference") describes x-y tiles that march along z with
-// planes staged in shared memory.  Here a 64 x 4 tile marches along z; at
-// every plane the workgroup computes z once per point of the tile plus its
-// upper x column and upper y row (65 x 5 points, two planes kept in LDS), and
-// every thread then reads z(i), z(i+e_x), z(i+e_y) from the current plane and
-// z(i+e_z) from the next one.  r is read through the caches; the voxel's own
-// r and r_z of the plane below are carried in registers.  The arithmetic is
-// the shared primal_z / dual_update pair, so the result is bit-identical to
-// the other variants.
+// "What made the difference") describes x-y tiles that march along z with two
+// planes of r and of z staged in shared memory.  Here a 64 x 4 tile marches
+// along z (8 planes per tile by default).  At every plane the workgroup
+// stages r of the next plane on the tile grown by its lower x column and
+// lower y row (66 x 6 points, 0 outside the volume: the lower-face rule of L),
+// computes z of the next plane once per point of the tile plus its upper x
+// column and upper y row (65 x 5 points) from the two staged r planes, and
+// then every thread updates its voxel from z(i), z(i+e_x), z(i+e_y) of the
+// current plane, z(i+e_z) of the next one and its own r of the current plane.
+// Three barriers per plane.  The arithmetic is the shared primal_z /
+// dual_update pair, so the result is bit-identical to the other variants.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,6 +26,8 @@ namespace tvfgp {
 
 constexpr int kZW = kTileX + 1;  // tile width plus the upper x column
 constexpr int kZH = kTileY + 1;  // tile height plus the upper y row
+constexpr int kRW = kTileX + 2;  // lower x column, tile, upper x column
+constexpr int kRH = kTileY + 2;  // lower y row, tile, upper y row
 
 template <typename I>
 __global__ __launch_bounds__(kBlock) void lds_march_kernel(
@@ -33,10 +37,13 @@ __global__ __launch_bounds__(kBlock) void lds_march_kernel(
     const float *__restrict__ ri2, float *__restrict__ ro0,
     float *__restrict__ ro1, float *__restrict__ ro2, float lam, float c,
     float m, Geometry<I> g) {
+  // r at tile coordinates (x, y) is rbuf[.][.][y + 1][x + 1], z is zbuf[.][y][x]
+  __shared__ float rbuf[2][3][kRH][kRW];
   __shared__ float zbuf[2][kZH][kZW];
-  const int lx = (int)(threadIdx.x % kTileX);
-  const int ly = (int)(threadIdx.x / kTileX);
-  // Halo point of this thread: wave 0 takes the upper y row, lanes 0..3 of
+  const int tid = (int)threadIdx.x;
+  const int lx = tid % kTileX;
+  const int ly = tid / kTileX;
+  // Halo z point of this thread: wave 0 takes the upper y row, lanes 0..3 of
   // wave 1 the upper x column; other threads have none.
   int hxl = -1, hyl = -1;
   if (ly == 0) {
@@ -64,58 +71,63 @@ __global__ __launch_bounds__(kBlock) void lds_march_kernel(
     const bool halo_ok = hxl >= 0 && hx < g.nx && hy < g.ny;
     const bool has_x = x + 1 < g.nx, has_y = y + 1 < g.ny;
 
+    // r of plane k on the staged region, 0 outside the volume
+    auto stage = [&](int slot, I k) {
+      for (int s = tid; s < kRW * kRH; s += kBlock) {
+        const int sx = s % kRW, sy2 = s / kRW;
+        const I gx = x0 + sx - 1, gy = y0 + sy2 - 1;
+        float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f;
+        if (gx >= 0 && gy >= 0 && gx < g.nx && gy < g.ny) {
+          const I j = gx + sy * gy + sz * k;
+          v0 = ri0[j];
+          v1 = ri1[j];
+          v2 = ri2[j];
+        }
+        rbuf[slot][0][sy2][sx] = v0;
+        rbuf[slot][1][sy2][sx] = v1;
+        rbuf[slot][2][sy2][sx] = v2;
+      }
+    };
+    // z of plane k at tile point (zx, zy) from staged r of plane k (slot) and
+    // r_z of plane k-1 (rz_lo, already 0 below the lower face)
+    auto z_at = [&](int slot, int zx, int zy, float bj, float rz_lo) {
+      const int sx = zx + 1, sy2 = zy + 1;
+      return primal_z(bj, rbuf[slot][0][sy2][sx], rbuf[slot][0][sy2][sx - 1],
+                      rbuf[slot][1][sy2][sx], rbuf[slot][1][sy2 - 1][sx],
+                      rbuf[slot][2][sy2][sx], rz_lo, lam);
+    };
+
     I i = own_ok ? x + sy * y + sz * z0 : 0;
     I ih = halo_ok ? hx + sy * hy + sz * z0 : 0;
-    float r0c = 0.0f, r1c = 0.0f, r2c = 0.0f, r2h = 0.0f;
     int cur = 0;
 
-    // z at the first plane
-    if (own_ok) {
-      r0c = ri0[i];
-      r1c = ri1[i];
-      r2c = ri2[i];
-      zbuf[0][ly][lx] = primal_z(b[i], r0c, load_or_zero(ri0, x > 0, i - 1, i),
-                                 r1c, load_or_zero(ri1, y > 0, i - sy, i), r2c,
-                                 load_or_zero(ri2, z0 > 0, i - sz, i), lam);
-    }
-    if (halo_ok) {
-      r2h = ri2[ih];
-      zbuf[0][hyl][hxl] = primal_z(
-          b[ih], ri0[ih], load_or_zero(ri0, hx > 0, ih - 1, ih), ri1[ih],
-          load_or_zero(ri1, hy > 0, ih - sy, ih), r2h,
-          load_or_zero(ri2, z0 > 0, ih - sz, ih), lam);
-    }
+    // plane z0: stage r, then z (r_z below from memory, 0 below the volume)
+    stage(0, z0);
+    __syncthreads();
+    if (own_ok)
+      zbuf[0][ly][lx] = z_at(0, lx, ly, b[i], load_or_zero(ri2, z0 > 0, i - sz, i));
+    if (halo_ok)
+      zbuf[0][hyl][hxl] = z_at(0, hxl, hyl, b[ih], load_or_zero(ri2, z0 > 0, ih - sz, ih));
 
     for (I k = z0; k < z1; ++k) {
       const int nxt = cur ^ 1;
       const bool has_z = k + 1 < g.nz;
-      // own p before the barrier, so its latency overlaps the z exchange
+      // own p before the barriers, so its latency overlaps the staging
       float pv0 = 0.0f, pv1 = 0.0f, pv2 = 0.0f;
       if (own_ok) {
         pv0 = p0[i];
         pv1 = p1[i];
         pv2 = p2[i];
       }
-      // z of the next plane; the own r loaded for it is next plane's own r
-      float r0n = 0.0f, r1n = 0.0f, r2n = 0.0f;
+      if (has_z) stage(nxt, k + 1);
+      __syncthreads();
+      // z of the next plane from the two staged r planes
       if (has_z) {
-        if (own_ok) {
-          const I j = i + sz;
-          r0n = ri0[j];
-          r1n = ri1[j];
-          r2n = ri2[j];
-          zbuf[nxt][ly][lx] = primal_z(
-              b[j], r0n, load_or_zero(ri0, x > 0, j - 1, j), r1n,
-              load_or_zero(ri1, y > 0, j - sy, j), r2n, r2c, lam);
-        }
-        if (halo_ok) {
-          const I jh = ih + sz;
-          const float r2hn = ri2[jh];
-          zbuf[nxt][hyl][hxl] = primal_z(
-              b[jh], ri0[jh], load_or_zero(ri0, hx > 0, jh - 1, jh), ri1[jh],
-              load_or_zero(ri1, hy > 0, jh - sy, jh), r2hn, r2h, lam);
-          r2h = r2hn;
-        }
+        if (own_ok)
+          zbuf[nxt][ly][lx] = z_at(nxt, lx, ly, b[i + sz], rbuf[cur][2][ly + 1][lx + 1]);
+        if (halo_ok)
+          zbuf[nxt][hyl][hxl] =
+              z_at(nxt, hxl, hyl, b[ih + sz], rbuf[cur][2][hyl + 1][hxl + 1]);
       }
       __syncthreads();
       if (own_ok) {
@@ -124,8 +136,9 @@ __global__ __launch_bounds__(kBlock) void lds_march_kernel(
         const float zy = zbuf[cur][ly + 1][lx];
         const float zz = zbuf[nxt][ly][lx];
         float o0, o1, o2;
-        dual_update(zc, zx, zy, zz, has_x, has_y, has_z, r0c, r1c, r2c, pv0,
-                    pv1, pv2, c, m, o0, o1, o2);
+        dual_update(zc, zx, zy, zz, has_x, has_y, has_z, rbuf[cur][0][ly + 1][lx + 1],
+                    rbuf[cur][1][ly + 1][lx + 1], rbuf[cur][2][ly + 1][lx + 1], pv0, pv1,
+                    pv2, c, m, o0, o1, o2);
         p0[i] = pv0;
         p1[i] = pv1;
         p2[i] = pv2;
@@ -133,11 +146,8 @@ __global__ __launch_bounds__(kBlock) void lds_march_kernel(
         ro1[i] = o1;
         ro2[i] = o2;
       }
-      // zbuf[cur] is rewritten as the next plane's "next" buffer
+      // rbuf[cur] and zbuf[cur] are rewritten as the next plane's "next"
       __syncthreads();
-      r0c = r0n;
-      r1c = r1n;
-      r2c = r2n;
       i += own_ok ? sz : 0;
       ih += halo_ok ? sz : 0;
       cur = nxt;

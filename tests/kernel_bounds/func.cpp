@@ -10,6 +10,7 @@
 // usage: func <kernel> <nx> <ny> <nz> <lambda> <m1> <m2> <dir> <wide:0|1> <grid:0=as launched>
 //   kernel: fused  one step (m1), p updated in place
 //           cube, cube_8x8x8  one step (m1) with the cube-tiled kernel
+//           lds_march  one step (m1) with the LDS z-march (8 planes per tile)
 //           tb2    two steps (m1 then m2) in one pass, p_in -> p_out
 //   dir holds b.bin (n floats), p.bin and r.bin (3n floats each); the kernel
 //   writes p_out.bin and r_out.bin there.
@@ -25,6 +26,7 @@
 #include "tv_fgp_fused_kernel.hpp"
 #include "tv_fgp_tb2_kernel.hpp"
 #include "tv_fgp_cube_kernel.hpp"
+#include "tv_fgp_lds_kernel.hpp"
 
 thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
 
@@ -109,6 +111,13 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
       tvfgp::fused_zx_kernel<I, Off, true, float>(b, p, p + n, p + 2 * n, r, r + n, r + 2 * n,
                                                   r_out, r_out + n, r_out + 2 * n, lam, c, m1,
                                                   g);
+    });
+    memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "lds_march")) {
+    const tvfgp::Geometry<I> g = tvfgp::make_geometry<I>(nx, ny, nz, 8);
+    run_grid(pick(g.ntiles, grid), tvfgp::kBlock, [&] {
+      tvfgp::lds_march_kernel<I>(b, p, p + n, p + 2 * n, r, r + n, r + 2 * n, r_out,
+                                 r_out + n, r_out + 2 * n, lam, c, m1, g);
     });
     memcpy(p_out, p, 3 * n * sizeof(float));
   } else if (!strcmp(kernel, "cube")) {

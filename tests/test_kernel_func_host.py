@@ -77,9 +77,10 @@ def test_fused_one_step(func, tmp_path):
     assert_bits(rg, re, "r")
 
 
-@pytest.mark.parametrize("kernel", ["cube", "cube_8x8x8"])
-@pytest.mark.parametrize("dims", [(37, 19, 11), (16, 8, 4), (1, 1, 1)], ids=lambda d: str(d))
-def test_cube_one_step(func, tmp_path, kernel, dims):
+@pytest.mark.parametrize("kernel", ["cube", "cube_8x8x8", "lds_march"])
+@pytest.mark.parametrize("dims", [(37, 19, 11), (16, 8, 4), (1, 1, 1), (70, 9, 19)],
+                         ids=lambda d: str(d))
+def test_lds_one_step(func, tmp_path, kernel, dims):
     b, p0, r0 = inputs(dims)
     pg, rg = emulate(func, tmp_path, kernel, b, p0, r0, 0.003, np.float32(0.4), 0.0)
     pe, re = oracle.step(b, p0, r0, 0.003, np.float32(0.4))
