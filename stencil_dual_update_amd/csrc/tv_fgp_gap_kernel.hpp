@@ -12,9 +12,12 @@
 //
 // z and g are computed in fp32 exactly as the step computes them (shared
 // primal_z, same boundary rule); the per-voxel terms and all sums are fp64.
-// The reduction is deterministic: a fixed number of workgroups each sum a
-// fixed set of tiles in a fixed order into one partial triple, and a single
-// workgroup adds the partials in a fixed order.
+// The first pass walks the volume like the default step kernel: 64 x 8 x-y
+// tiles marching 4 planes along z, z computed once per point (tile plus its
+// upper x column and y row) into a ring of three LDS planes, z(i+e_x) and
+// z(i+e_y) read from LDS.  The reduction is deterministic: a fixed number of
+// workgroups each sum a fixed set of tiles in a fixed order into one partial
+// triple, and a single workgroup adds the partials in a fixed order.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -22,13 +25,13 @@
 #include <stdint.h>
 
 #include "tv_fgp_device.hpp"
+#include "tv_fgp_fused_kernel.hpp"
 
 #pragma clang fp contract(off)
 
 namespace tvfgp {
 
 constexpr int kGapGrid = 1024;    // partial triples (upper bound)
-constexpr int kGapPlanes = 8;     // planes per tile
 constexpr int kGapFinalBlock = 256;
 
 // Per-voxel contribution: |g|, |g| - g.p and 1/2 (z - b)^2, in fp64.
@@ -66,73 +69,140 @@ __device__ __forceinline__ void block_sum3(double &a, double &b, double &c,
   c = sh[2][0];
 }
 
-// Pass 1: each workgroup walks tiles t = blockIdx.x, blockIdx.x + gridDim.x,
-// ... (64 x 4 x kGapPlanes voxels each); each thread walks its column along
-// z, carrying z and p of the plane above.  Writes partial[3*blockIdx.x + k].
-template <typename I>
-__global__ __launch_bounds__(kBlock) void gap_partial_kernel(
+// Pass 1: workgroup w walks tiles w, w + gridDim.x, ... (64 x 8 x 4 voxels
+// each) and writes the sum of its voxels' terms to partial[3w .. 3w+2].
+template <typename I, typename Off>
+__global__ __launch_bounds__(kZxBlock) void gap_partial_kernel(
     const float *__restrict__ b, const float *__restrict__ p0,
     const float *__restrict__ p1, const float *__restrict__ p2, float lam,
-    Geometry<I> g, double *__restrict__ partial) {
-  __shared__ double sh[3][kBlock];
-  const I lx = (I)(threadIdx.x % kTileX);
-  const I ly = (I)(threadIdx.x / kTileX);
+    ZxGeometry<I, Off> g, double *__restrict__ partial) {
+  constexpr int kW = kZxTileX + 1, kH = kZxTileY + 1;
+  __shared__ float zring[3][kH][kW];
+  __shared__ double sh[3][kZxBlock];
+  const int lx = (int)(threadIdx.x % kZxTileX);
+  const int ly = (int)(threadIdx.x / kZxTileX);
+  // halo z point: wave 0 the upper y row, lanes 0..7 of wave 1 the upper x column
+  int hxl = -1, hyl = -1;
+  if (ly == 0) {
+    hxl = lx;
+    hyl = kZxTileY;
+  } else if (ly == 1 && lx < kZxTileY) {
+    hxl = kZxTileX;
+    hyl = lx;
+  }
+  const Off sy4 = g.sy4, sz4 = g.sz4;
+  const Off four = 4;
   double s_norm = 0.0, s_gap = 0.0, s_fid = 0.0;
+
   for (I t = (I)blockIdx.x; t < g.ntiles; t += (I)gridDim.x) {
-    const I tx = t % g.tiles_x;
-    const I rest = t / g.tiles_x;
-    const I ty = rest % g.tiles_y;
-    const I tz = rest / g.tiles_y;
-    const I x = tx * kTileX + lx;
-    const I y = ty * kTileY + ly;
-    if (x >= g.nx || y >= g.ny) continue;
+    I tx, ty, tz;
+    ordered_tile<I, Off>(xcd_tile(t, g.ntiles), g, tx, ty, tz);
+    const I x0 = tx * kZxTileX, y0 = ty * kZxTileY;
     const I z0 = tz * g.planes;
     const I z1 = (z0 + g.planes < g.nz) ? z0 + g.planes : g.nz;
+    const I x = x0 + lx, y = y0 + ly;
+    const I hx = x0 + hxl, hy = y0 + hyl;
+    const bool own_ok = x < g.nx && y < g.ny;
+    const bool halo_ok = hxl >= 0 && hx < g.nx && hy < g.ny;
     const bool has_x = x + 1 < g.nx, has_y = y + 1 < g.ny;
     const bool low_x = x > 0, low_y = y > 0;
-    const I sy = g.sy, sz = g.sz;
-    I i = x + sy * y + sz * z0;
-    float pc0 = p0[i], pc1 = p1[i], pc2 = p2[i];
-    float bc = b[i];
-    float zc = primal_z(bc, pc0, load_or_zero(p0, low_x, i - 1, i), pc1,
-                        load_or_zero(p1, low_y, i - sy, i), pc2,
-                        load_or_zero(p2, z0 > 0, i - sz, i), lam);
-    const I ixs = has_x ? i + 1 : i;
-    const I iys = has_y ? i + sy : i;
-    float p2x_lo = load_or_zero(p2, z0 > 0, ixs - sz, ixs);
-    float p2y_lo = load_or_zero(p2, z0 > 0, iys - sz, iys);
-    for (I zp = z0; zp < z1; ++zp, i += sz) {
-      const bool has_z = zp + 1 < g.nz;
-      const I ix = has_x ? i + 1 : i;
-      const float p2x = p2[ix];
-      const float zx = primal_z(b[ix], p0[ix], pc0, p1[ix],
-                                load_or_zero(p1, low_y, ix - sy, ix), p2x, p2x_lo, lam);
-      p2x_lo = p2x;
-      const I iy = has_y ? i + sy : i;
-      const float p2y = p2[iy];
-      const float zy = primal_z(b[iy], p0[iy], load_or_zero(p0, low_x, iy - 1, iy),
-                                p1[iy], pc1, p2y, p2y_lo, lam);
-      p2y_lo = p2y;
-      const I iz = has_z ? i + sz : i;
-      const float bz = b[iz], pz0 = p0[iz], pz1 = p1[iz], pz2 = p2[iz];
-      const float zz = primal_z(bz, pz0, load_or_zero(p0, low_x, iz - 1, iz), pz1,
-                                load_or_zero(p1, low_y, iz - sy, iz), pz2, pc2, lam);
-      const float gx = has_x ? zc - zx : 0.0f;
-      const float gy = has_y ? zc - zy : 0.0f;
-      const float gz = has_z ? zc - zz : 0.0f;
-      double n, gp, f;
-      gap_terms(gx, gy, gz, pc0, pc1, pc2, zc, bc, n, gp, f);
-      s_norm = s_norm + n;
-      s_gap = s_gap + gp;
-      s_fid = s_fid + f;
-      zc = zz;
-      bc = bz;
-      pc0 = pz0;
-      pc1 = pz1;
-      pc2 = pz2;
+    const bool hlow_x = hx > 0, hlow_y = hy > 0;
+    const bool low_z = z0 > 0;
+    const Off oi = own_ok ? ((Off)x + (Off)g.nx * (Off)y) * four + (Off)z0 * sz4 : 0;
+    const Off oh = halo_ok ? ((Off)hx + (Off)g.nx * (Off)hy) * four + (Off)z0 * sz4 : 0;
+
+    // z at plane z0; the own p and b of the column are carried
+    float pc0 = 0.0f, pc1 = 0.0f, pc2 = 0.0f, bc = 0.0f, ph2 = 0.0f, zc = 0.0f;
+    if (own_ok) {
+      pc0 = ld(p0, oi);
+      pc1 = ld(p1, oi);
+      pc2 = ld(p2, oi);
+      bc = ld(b, oi);
+      const float a = ld(p0, low_x ? oi - four : oi);
+      const float e = ld(p1, low_y ? oi - sy4 : oi);
+      const float f = ld(p2, low_z ? oi - sz4 : oi);
+      zc = primal_z(bc, pc0, low_x ? a : 0.0f, pc1, low_y ? e : 0.0f, pc2,
+                    low_z ? f : 0.0f, lam);
+      zring[0][ly][lx] = zc;
     }
+    if (halo_ok) {
+      ph2 = ld(p2, oh);
+      const float a = ld(p0, hlow_x ? oh - four : oh);
+      const float e = ld(p1, hlow_y ? oh - sy4 : oh);
+      const float f = ld(p2, low_z ? oh - sz4 : oh);
+      zring[0][hyl][hxl] = primal_z(ld(b, oh), ld(p0, oh), hlow_x ? a : 0.0f, ld(p1, oh),
+                                    hlow_y ? e : 0.0f, ph2, low_z ? f : 0.0f, lam);
+    }
+
+    // loads of the next plane (own point and halo point)
+    float nb = 0.0f, n0 = 0.0f, n1 = 0.0f, n2 = 0.0f, n0l = 0.0f, n1l = 0.0f;
+    float hb = 0.0f, h0 = 0.0f, h1 = 0.0f, h2 = 0.0f, h0l = 0.0f, h1l = 0.0f;
+    auto load_plane = [&](I kp) {
+      const Off dz = (Off)(kp - z0) * sz4;
+      if (own_ok) {
+        const Off j = oi + dz;
+        nb = ld(b, j);
+        n0 = ld(p0, j);
+        n1 = ld(p1, j);
+        n2 = ld(p2, j);
+        n0l = ld(p0, low_x ? j - four : j);
+        n1l = ld(p1, low_y ? j - sy4 : j);
+      }
+      if (halo_ok) {
+        const Off j = oh + dz;
+        hb = ld(b, j);
+        h0 = ld(p0, j);
+        h1 = ld(p1, j);
+        h2 = ld(p2, j);
+        h0l = ld(p0, hlow_x ? j - four : j);
+        h1l = ld(p1, hlow_y ? j - sy4 : j);
+      }
+    };
+    if (z0 + 1 < g.nz) load_plane(z0 + 1);
+
+    int cur = 0;
+    for (I k = z0; k < z1; ++k) {
+      const int nxt = cur == 2 ? 0 : cur + 1;
+      const bool has_z = k + 1 < g.nz;
+      const float cb = nb, c0 = n0, c1 = n1, c2 = n2, c0l = n0l, c1l = n1l;
+      const float db = hb, d0 = h0, d1 = h1, d2 = h2, d0l = h0l, d1l = h1l;
+      if (k + 1 < z1 && k + 2 < g.nz) load_plane(k + 2);
+      float zz = 0.0f;
+      if (has_z) {
+        if (own_ok) {
+          zz = primal_z(cb, c0, low_x ? c0l : 0.0f, c1, low_y ? c1l : 0.0f, c2, pc2, lam);
+          zring[nxt][ly][lx] = zz;
+        }
+        if (halo_ok) {
+          zring[nxt][hyl][hxl] = primal_z(db, d0, hlow_x ? d0l : 0.0f, d1,
+                                          hlow_y ? d1l : 0.0f, d2, ph2, lam);
+          ph2 = d2;
+        }
+      }
+      // ring of three planes: one barrier per plane (as in the step kernel)
+      __syncthreads();
+      if (own_ok) {
+        const float zx = zring[cur][ly][lx + 1];
+        const float zy = zring[cur][ly + 1][lx];
+        const float gx = has_x ? zc - zx : 0.0f;
+        const float gy = has_y ? zc - zy : 0.0f;
+        const float gz = has_z ? zc - zz : 0.0f;
+        double n, gp, f;
+        gap_terms(gx, gy, gz, pc0, pc1, pc2, zc, bc, n, gp, f);
+        s_norm = s_norm + n;
+        s_gap = s_gap + gp;
+        s_fid = s_fid + f;
+      }
+      zc = zz;
+      bc = cb;
+      pc0 = c0;
+      pc1 = c1;
+      pc2 = c2;
+      cur = nxt;
+    }
+    __syncthreads();  // the next tile rewrites ring slot 0
   }
-  block_sum3<kBlock>(s_gap, s_norm, s_fid, sh);
+  block_sum3<kZxBlock>(s_gap, s_norm, s_fid, sh);
   if (threadIdx.x == 0) {
     partial[3 * blockIdx.x + 0] = s_gap;
     partial[3 * blockIdx.x + 1] = s_norm;
@@ -160,10 +230,10 @@ __global__ __launch_bounds__(kGapFinalBlock) void gap_final_kernel(
   }
 }
 
-// Number of partial triples for these dimensions.
+// Number of partial triples (= workgroups of pass 1) for these dimensions.
 inline int gap_grid(int64_t nx, int64_t ny, int64_t nz) {
-  const int64_t tiles = ((nx + kTileX - 1) / kTileX) * ((ny + kTileY - 1) / kTileY) *
-                        ((nz + kGapPlanes - 1) / kGapPlanes);
+  const int64_t tiles = ((nx + kZxTileX - 1) / kZxTileX) * ((ny + kZxTileY - 1) / kZxTileY) *
+                        ((nz + kZxPlanes - 1) / kZxPlanes);
   return (int)(tiles < kGapGrid ? tiles : kGapGrid);
 }
 

@@ -20,6 +20,8 @@
 #include <string.h>
 #include <sys/mman.h>
 
+#include <type_traits>
+
 #include "tv_fgp_ablation_kernels.hpp"
 #include "tv_fgp_device.hpp"
 #include "tv_fgp_fused_kernel.hpp"
@@ -189,12 +191,13 @@ void run_ablation(const char *variant, const Bufs &v, int64_t nx, int64_t ny, in
                        v.ro[1], v.ro[2], 8.3f, 0.5f, g);
       });
   } else if (!strcmp(variant, "gap")) {
-    const Geometry<I> g = make_geometry<I>(nx, ny, nz, kGapPlanes);
+    typedef typename std::conditional<sizeof(I) == 4, uint32_t, uint64_t>::type Off;
+    const ZxGeometry<I, Off> g = zx_geometry<I, Off>(nx, ny, nz);
     const int count = grid ? (int)grid : gap_grid(nx, ny, nz);
     double *partial = (double *)guarded((size_t)count * 3 * sizeof(double), true, 99);
     double *out = (double *)guarded(3 * sizeof(double), true, 98);
-    run_grid((unsigned)count, kBlock, [&] {
-      gap_partial_kernel<I>(v.b, v.p[0], v.p[1], v.p[2], 0.01f, g, partial);
+    run_grid((unsigned)count, kZxBlock, [&] {
+      gap_partial_kernel<I, Off>(v.b, v.p[0], v.p[1], v.p[2], 0.01f, g, partial);
     });
     run_grid(1, kGapFinalBlock, [&] { gap_final_kernel(partial, count, 0.01, out); });
   } else if (!strcmp(variant, "lds_march")) {

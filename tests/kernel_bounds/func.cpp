@@ -11,6 +11,7 @@
 //   kernel: fused  one step (m1), p updated in place
 //           cube, cube_8x8x8  one step (m1) with the cube-tiled kernel
 //           lds_march  one step (m1) with the LDS z-march (8 planes per tile)
+//           gap    duality gap of p (three doubles written to <dir>/gap.bin)
 //           tb2    two steps (m1 then m2) in one pass, p_in -> p_out
 //   dir holds b.bin (n floats), p.bin and r.bin (3n floats each); the kernel
 //   writes p_out.bin and r_out.bin there.
@@ -27,6 +28,7 @@
 #include "tv_fgp_tb2_kernel.hpp"
 #include "tv_fgp_cube_kernel.hpp"
 #include "tv_fgp_lds_kernel.hpp"
+#include "tv_fgp_gap_kernel.hpp"
 
 thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
 
@@ -102,7 +104,8 @@ unsigned pick(int64_t ntiles, unsigned grid) {
 
 template <typename I, typename Off>
 void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, float m1, float m2,
-         unsigned grid, const float *b, float *p, float *r, float *p_out, float *r_out) {
+         unsigned grid, const float *b, float *p, float *r, float *p_out, float *r_out,
+         const std::string &dir) {
   const size_t n = (size_t)(nx * ny * nz);
   const float c = 1.0f / (12.0f * lam);
   if (!strcmp(kernel, "fused")) {
@@ -113,6 +116,23 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
                                                   g);
     });
     memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "gap")) {
+    // duality gap of p: the three sums go to <dir>/gap.bin as doubles
+    const auto g = tvfgp::zx_geometry<I, Off>(nx, ny, nz);
+    const int count = grid ? (int)grid : tvfgp::gap_grid(nx, ny, nz);
+    std::vector<double> partial((size_t)count * 3);
+    run_grid((unsigned)count, tvfgp::kZxBlock, [&] {
+      tvfgp::gap_partial_kernel<I, Off>(b, p, p + n, p + 2 * n, lam, g, partial.data());
+    });
+    double out[3];
+    run_grid(1, tvfgp::kGapFinalBlock,
+             [&] { tvfgp::gap_final_kernel(partial.data(), count, (double)lam, out); });
+    FILE *f = fopen((dir + "/gap.bin").c_str(), "wb");
+    if (!f || fwrite(out, sizeof(double), 3, f) != 3) {
+      fprintf(stderr, "cannot write gap.bin\n");
+      exit(3);
+    }
+    fclose(f);
   } else if (!strcmp(kernel, "lds_march")) {
     const tvfgp::Geometry<I> g = tvfgp::make_geometry<I>(nx, ny, nz, 8);
     run_grid(pick(g.ntiles, grid), tvfgp::kBlock, [&] {
@@ -168,10 +188,10 @@ int main(int argc, char **argv) {
   std::vector<float> p_out(3 * n, -12345.0f), r_out(3 * n, -12345.0f);
   if (wide)
     run<int64_t, uint64_t>(kernel, nx, ny, nz, lam, m1, m2, grid, b.data(), p.data(),
-                           r.data(), p_out.data(), r_out.data());
+                           r.data(), p_out.data(), r_out.data(), dir);
   else
     run<int32_t, uint32_t>(kernel, nx, ny, nz, lam, m1, m2, grid, b.data(), p.data(),
-                           r.data(), p_out.data(), r_out.data());
+                           r.data(), p_out.data(), r_out.data(), dir);
   write_file(dir + "/p_out.bin", p_out);
   write_file(dir + "/r_out.bin", r_out);
   printf("ok %s %lldx%lldx%lld\n", kernel, (long long)nx, (long long)ny, (long long)nz);

@@ -88,6 +88,27 @@ def test_lds_one_step(func, tmp_path, kernel, dims):
     assert_bits(rg, re, "r")
 
 
+@pytest.mark.parametrize("dims,grid", [((67, 19, 11), 0), ((130, 17, 9), 3), ((1, 1, 1), 0)],
+                         ids=lambda c: str(c))
+def test_duality_gap(func, tmp_path, dims, grid):
+    """The gap reduction's z exchange through LDS: sums within fp64 rounding of the oracle."""
+    b, p0, r0 = inputs(dims)
+    lam = 0.003
+    d = str(tmp_path)
+    nz, ny, nx = b.shape
+    b.tofile(os.path.join(d, "b.bin"))
+    p0.tofile(os.path.join(d, "p.bin"))
+    r0.tofile(os.path.join(d, "r.bin"))
+    r = subprocess.run([func, "gap", str(nx), str(ny), str(nz), repr(lam), "0", "0", d, "0",
+                        str(grid)], capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0, r.stderr
+    got = np.fromfile(os.path.join(d, "gap.bin"), np.float64)
+    g, tv, fid = oracle.duality_gap(b, p0, lam)
+    assert abs(got[0] - g) <= 1e-10 * lam * tv
+    assert abs(got[1] - tv) <= 1e-10 * tv
+    assert abs(got[2] - fid) <= 1e-10 * max(fid, 1e-300)
+
+
 # (dims, 64-bit path, forced grid): slab ends, ragged x/y tails, nz below one
 # slab, one voxel, tiles looped over by a short grid
 CASES = [((65, 9, 17), 0, 0), ((64, 8, 48), 1, 0), ((130, 17, 33), 0, 3), ((1, 1, 40), 0, 0),
