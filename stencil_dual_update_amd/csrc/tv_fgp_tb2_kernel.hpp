@@ -50,7 +50,7 @@ namespace tvfgp {
 constexpr int kTbTileX = 64;
 constexpr int kTbTileY = 8;
 constexpr int kTbBlock = kTbTileX * kTbTileY;
-constexpr int kTbPlanes = 32;    // output planes per tile
+constexpr int kTbPlanes = 32;    // output planes per tile (most; see tb_planes)
 constexpr int kTbGroupMax = 16;  // tile columns per group in the tile order
 constexpr int kTbReach = 64;     // tiles whose reads one XCD's L2 holds
 constexpr int kTbR0X = kTbTileX + 3, kTbR0Y = kTbTileY + 3;
@@ -319,8 +319,22 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
   }
 }
 
+// Planes per slab: the largest of 32 and 16 that still gives at least 1536
+// tiles (two per workgroup slot of the chip at three workgroups per CU), else
+// 8.  A slab re-reads 4 planes and runs 4 pipeline-filling iterations, so
+// long slabs pay off on large volumes; small volumes need the tiles to fill
+// the chip.  Measured best at 512^3 (32), 256^3 (16) and 128^3 (8).
+inline int64_t tb_planes(int64_t nx, int64_t ny, int64_t nz) {
+  const int64_t txy = ((nx + kTbTileX - 1) / kTbTileX) * ((ny + kTbTileY - 1) / kTbTileY);
+  for (int64_t p = kTbPlanes; p >= 16; p /= 2)
+    if (txy * ((nz + p - 1) / p) >= 1536) return p;
+  return 8;
+}
+
+// planes <= 0: tb_planes()
 template <typename I, typename Off>
-inline ZxGeometry<I, Off> tb_geometry(int64_t nx, int64_t ny, int64_t nz) {
+inline ZxGeometry<I, Off> tb_geometry(int64_t nx, int64_t ny, int64_t nz, int64_t planes = 0) {
+  if (planes <= 0) planes = tb_planes(nx, ny, nz);
   ZxGeometry<I, Off> g;
   g.nx = (I)nx;
   g.ny = (I)ny;
@@ -329,8 +343,8 @@ inline ZxGeometry<I, Off> tb_geometry(int64_t nx, int64_t ny, int64_t nz) {
   g.sz4 = (Off)nx * (Off)ny * 4;
   g.tiles_x = (I)((nx + kTbTileX - 1) / kTbTileX);
   g.tiles_y = (I)((ny + kTbTileY - 1) / kTbTileY);
-  g.planes = (I)kTbPlanes;
-  g.tiles_z = (I)((nz + kTbPlanes - 1) / kTbPlanes);
+  g.planes = (I)planes;
+  g.tiles_z = (I)((nz + planes - 1) / planes);
   g.ntiles = g.tiles_x * g.tiles_y * g.tiles_z;
   g.group = g.tiles_x < (I)kTbGroupMax ? g.tiles_x : (I)kTbGroupMax;
   const I band = (I)kTbReach / g.group;

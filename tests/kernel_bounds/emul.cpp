@@ -84,8 +84,8 @@ struct Bufs {
 };
 
 template <typename I, typename Off>
-void run_tb2(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid) {
-  const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz);
+void run_tb2(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid, int64_t planes) {
+  const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz, planes);
   run_grid(pick_grid(g.ntiles, grid), tvfgp::kTbBlock, [&] {
     tvfgp::tb2_kernel<I, Off>(v.b, v.p[0], v.p[1], v.p[2], v.po[0], v.po[1], v.po[2], v.ri[0],
                               v.ri[1], v.ri[2], v.ro[0], v.ro[1], v.ro[2], 0.01f, 8.3f, 0.3f,
@@ -247,9 +247,9 @@ int main(int argc, char **argv) {
       run_fused<int32_t, uint32_t, float>(v, nx, ny, nz, grid, sp);
   } else if (!strcmp(variant, "tb2")) {
     if (wide)
-      run_tb2<int64_t, uint64_t>(v, nx, ny, nz, grid);
+      run_tb2<int64_t, uint64_t>(v, nx, ny, nz, grid, planes);
     else
-      run_tb2<int32_t, uint32_t>(v, nx, ny, nz, grid);
+      run_tb2<int32_t, uint32_t>(v, nx, ny, nz, grid, planes);
   } else if (!strncmp(variant, "pair", 4)) {
     const bool sp = strstr(variant, "nostream") == nullptr;
     if (nx % 2 != 0) {

@@ -8,6 +8,7 @@
 // GPU, so results can be compared bit for bit with the CPU oracle.
 //
 // usage: func <kernel> <nx> <ny> <nz> <lambda> <m1> <m2> <dir> <wide:0|1> <grid:0=as launched>
+//             [planes: tb2 slab length, 0 = as launched]
 //   kernel: fused  one step (m1), p updated in place
 //           cube, cube_8x8x8  one step (m1) with the cube-tiled kernel
 //           lds_march  one step (m1) with the LDS z-march (8 planes per tile)
@@ -105,7 +106,7 @@ unsigned pick(int64_t ntiles, unsigned grid) {
 template <typename I, typename Off>
 void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, float m1, float m2,
          unsigned grid, const float *b, float *p, float *r, float *p_out, float *r_out,
-         const std::string &dir) {
+         const std::string &dir, int64_t planes) {
   const size_t n = (size_t)(nx * ny * nz);
   const float c = 1.0f / (12.0f * lam);
   if (!strcmp(kernel, "fused")) {
@@ -155,7 +156,7 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
     });
     memcpy(p_out, p, 3 * n * sizeof(float));
   } else if (!strcmp(kernel, "tb2")) {
-    const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz);
+    const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz, planes);
     run_grid(pick(g.ntiles, grid), tvfgp::kTbBlock, [&] {
       tvfgp::tb2_kernel<I, Off>(b, p, p + n, p + 2 * n, p_out, p_out + n, p_out + 2 * n, r,
                                 r + n, r + 2 * n, r_out, r_out + n, r_out + 2 * n, lam, c, m1,
@@ -170,10 +171,11 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
 }  // namespace
 
 int main(int argc, char **argv) {
-  if (argc != 11) {
-    fprintf(stderr, "usage: func kernel nx ny nz lambda m1 m2 dir wide grid\n");
+  if (argc != 11 && argc != 12) {
+    fprintf(stderr, "usage: func kernel nx ny nz lambda m1 m2 dir wide grid [planes]\n");
     return 2;
   }
+  const int64_t planes = argc == 12 ? atoll(argv[11]) : 0;
   const char *kernel = argv[1];
   const int64_t nx = atoll(argv[2]), ny = atoll(argv[3]), nz = atoll(argv[4]);
   const float lam = strtof(argv[5], nullptr), m1 = strtof(argv[6], nullptr),
@@ -188,10 +190,10 @@ int main(int argc, char **argv) {
   std::vector<float> p_out(3 * n, -12345.0f), r_out(3 * n, -12345.0f);
   if (wide)
     run<int64_t, uint64_t>(kernel, nx, ny, nz, lam, m1, m2, grid, b.data(), p.data(),
-                           r.data(), p_out.data(), r_out.data(), dir);
+                           r.data(), p_out.data(), r_out.data(), dir, planes);
   else
     run<int32_t, uint32_t>(kernel, nx, ny, nz, lam, m1, m2, grid, b.data(), p.data(),
-                           r.data(), p_out.data(), r_out.data(), dir);
+                           r.data(), p_out.data(), r_out.data(), dir, planes);
   write_file(dir + "/p_out.bin", p_out);
   write_file(dir + "/r_out.bin", r_out);
   printf("ok %s %lldx%lldx%lld\n", kernel, (long long)nx, (long long)ny, (long long)nz);

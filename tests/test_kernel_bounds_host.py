@@ -54,7 +54,8 @@ def test_every_access_in_bounds(emul, variant):
         for wide in (0, 1):
             for end in (0, 1):
                 for grid in ((0, 7) if wide else (0,)):
-                    for planes in ((8, 3) if variant not in FOUR_PLANE else (4,)):
+                    for planes in ((8, 16, 32) if variant == "tb2" else
+                                   (8, 3) if variant not in FOUR_PLANE else (4,)):
                         args = [emul, variant, str(nx), str(ny), str(nz), str(wide), str(grid),
                                 str(end), str(planes)]
                         r = subprocess.run(args, capture_output=True, text=True, timeout=120)

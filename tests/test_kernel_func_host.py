@@ -41,14 +41,14 @@ def func(tmp_path_factory):
     return out
 
 
-def emulate(func, tmp_path, kernel, b, p0, r0, lam, m1, m2, wide=0, grid=0):
+def emulate(func, tmp_path, kernel, b, p0, r0, lam, m1, m2, wide=0, grid=0, planes=0):
     nz, ny, nx = b.shape
     d = str(tmp_path)
     b.tofile(os.path.join(d, "b.bin"))
     p0.tofile(os.path.join(d, "p.bin"))
     r0.tofile(os.path.join(d, "r.bin"))
     r = subprocess.run([func, kernel, str(nx), str(ny), str(nz), repr(lam), repr(float(m1)),
-                        repr(float(m2)), d, str(wide), str(grid)],
+                        repr(float(m2)), d, str(wide), str(grid), str(planes)],
                        capture_output=True, text=True, timeout=300)
     assert r.returncode == 0 and r.stdout.startswith("ok"), r.stderr
     pg = np.fromfile(os.path.join(d, "p_out.bin"), np.float32).reshape(p0.shape)
@@ -109,17 +109,19 @@ def test_duality_gap(func, tmp_path, dims, grid):
     assert abs(got[2] - fid) <= 1e-10 * max(fid, 1e-300)
 
 
-# (dims, 64-bit path, forced grid): slab ends, ragged x/y tails, nz below one
-# slab, one voxel, tiles looped over by a short grid
-CASES = [((65, 9, 17), 0, 0), ((64, 8, 48), 1, 0), ((130, 17, 33), 0, 3), ((1, 1, 40), 0, 0),
-         ((5, 70, 3), 0, 0), ((63, 7, 15), 0, 0), ((1, 1, 1), 0, 0), ((66, 10, 18), 1, 2)]
+# (dims, 64-bit path, forced grid, slab length; 0 = as launched): slab ends,
+# ragged x/y tails, nz below one slab, one voxel, tiles looped over by a short
+# grid, each slab length the launcher picks
+CASES = [((65, 9, 17), 0, 0, 0), ((64, 8, 48), 1, 0, 16), ((130, 17, 33), 0, 3, 0),
+         ((1, 1, 40), 0, 0, 32), ((5, 70, 3), 0, 0, 0), ((63, 7, 15), 0, 0, 0), ((1, 1, 1), 0, 0, 0),
+         ((66, 10, 18), 1, 2, 16), ((64, 8, 70), 0, 0, 32)]
 
 
-@pytest.mark.parametrize("dims,wide,grid", CASES, ids=lambda c: str(c))
-def test_two_steps_per_pass(func, tmp_path, dims, wide, grid):
+@pytest.mark.parametrize("dims,wide,grid,planes", CASES, ids=lambda c: str(c))
+def test_two_steps_per_pass(func, tmp_path, dims, wide, grid, planes):
     b, p0, r0 = inputs(dims)
     m1, m2 = np.float32(0.3), np.float32(0.61)
-    pg, rg = emulate(func, tmp_path, "tb2", b, p0, r0, 0.003, m1, m2, wide, grid)
+    pg, rg = emulate(func, tmp_path, "tb2", b, p0, r0, 0.003, m1, m2, wide, grid, planes)
     pe, re = oracle.step(b, p0, r0, 0.003, m1)
     pe, re = oracle.step(b, pe, re, 0.003, m2)
     assert_bits(pg, pe, "p %s" % (dims,))
