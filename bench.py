@@ -160,7 +160,7 @@ def parse():
 def main():
     args = parse()
     if args.variant is None:
-        args.variant = "fused" if args.storage == "half" else "tb2"
+        args.variant = "tb2"
     if args.traffic:
         write_traffic(*args.traffic, args.variant)
         return 0
@@ -184,8 +184,9 @@ def main():
     n_inner = w["n_inner"]
     variant = tvf.VARIANTS[args.variant]
     half = args.storage == "half"
-    if half and args.variant != "fused":
-        print("--storage half runs the fused kernel only", file=sys.stderr)
+    if half and args.variant not in ("fused", "tb2"):
+        print("--storage half runs the one-step (fused) or two-steps-per-pass (tb2) kernels",
+              file=sys.stderr)
         return 2
     nvox = nx * ny * nz
 
@@ -200,11 +201,13 @@ def main():
     rb = torch.empty_like(ra)
     ws = (torch.empty_like(b) if variant == tvf.TWO_KERNEL else
           torch.empty_like(p) if variant == tvf.TB2 else None)
-    spl = 1 if half else STEPS_PER_LAUNCH.get(args.variant, 1)
+    spl = STEPS_PER_LAUNCH.get(args.variant, 1)
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
     def run(r_cur, r_nxt, n_outer, ni):
+        if half and spl == 2:
+            return tvf.tv_fgp_run2_h(b, p, ws, r_cur, r_nxt, lam, n_outer, ni, stream=stream)
         if half:
             return tvf.tv_fgp_run_h(b, p, r_cur, r_nxt, lam, n_outer, ni, stream=stream)
         return tvf.tv_fgp_run(b, p, r_cur, r_nxt, lam, n_outer, ni, variant=variant, z_ws=ws,
@@ -250,9 +253,9 @@ def main():
             k = q * spl
             evs[q][0].record(stream)
             if spl == 2:
-                tvf.tv_fgp_step2(b, p_cur, p_alt, r_cur, r_nxt, lam,
-                                 tvf.momentum(k % n_inner + 1),
-                                 tvf.momentum((k + 1) % n_inner + 1), stream=stream)
+                step2 = tvf.tv_fgp_step2_h if half else tvf.tv_fgp_step2
+                step2(b, p_cur, p_alt, r_cur, r_nxt, lam, tvf.momentum(k % n_inner + 1),
+                      tvf.momentum((k + 1) % n_inner + 1), stream=stream)
                 p_cur, p_alt = p_alt, p_cur
             else:
                 step(r_cur, r_nxt, tvf.momentum(k % n_inner + 1))
@@ -277,16 +280,22 @@ def main():
                    for _ in range(n1 + 5)]
             for q in range(n1 + 5):
                 ev1[q][0].record(stream)
-                tvf.tv_fgp_step(b, p, r_cur, r_nxt, lam, tvf.momentum(q % n_inner + 1),
-                                stream=stream)
+                m = tvf.momentum(q % n_inner + 1)
+                if half:
+                    tvf.tv_fgp_step_h(b, p, r_cur, r_nxt, lam, m, stream=stream)
+                else:
+                    tvf.tv_fgp_step(b, p, r_cur, r_nxt, lam, m, stream=stream)
                 ev1[q][1].record(stream)
                 r_cur, r_nxt = r_nxt, r_cur
             torch.cuda.synchronize()
         ms1 = float(np.mean([e0.elapsed_time(e1) for e0, e1 in ev1[5:]]))
-        gbs1 = 52 * nvox / (ms1 * 1e-3) / 1e9
-        one_step = {"kernel": "fused_zx_kernel", "ms_per_step": round(ms1, 5),
-                    "achieved_gbps": round(gbs1, 1), "frac": round(gbs1 / HBM_PEAK_GBS, 4),
-                    "traffic": None if args.dims else measured_traffic("fused", args.workload),
+        bpv1 = BYTES_PER_VOXEL_HALF if half else 52
+        gbs1 = bpv1 * nvox / (ms1 * 1e-3) / 1e9
+        one_step = {"kernel": "fused_pair_kernel (binary16)" if half else "fused_zx_kernel",
+                    "ms_per_step": round(ms1, 5), "achieved_gbps": round(gbs1, 1),
+                    "frac": round(gbs1 / HBM_PEAK_GBS, 4),
+                    "traffic": None if (args.dims or half) else
+                    measured_traffic("fused", args.workload),
                     "launches": n1}
 
     # duality-gap reduction (reads b and p: 16 B per voxel), of the fp32 dual

@@ -203,6 +203,31 @@ int tv_fgp_run_h(const float *b, uint16_t *const p[3], uint16_t *const r_a[3],
                  uint16_t *const r_b[3], float lambda, int n_outer, int n_inner,
                  int64_t nx, int64_t ny, int64_t nz, void *stream, int *r_final);
 
+/*
+ * tv_fgp_step2 with the binary16 dual of tv_fgp_step_h: two steps in one
+ * pass, each step's p and r rounded to binary16 as tv_fgp_step_h rounds them
+ * (the first step's rounded p' and r' feed the second), so the result equals
+ * two tv_fgp_step_h calls bit for bit.  p_in and p_out must be separate
+ * buffers (the pass reads p_in around each tile while others write p_out).
+ * Binary16 volumes 2-byte aligned; status codes as tv_fgp_step2.
+ */
+int tv_fgp_step2_h(const float *b, const uint16_t *const p_in[3], uint16_t *const p_out[3],
+                   const uint16_t *const r_in[3], uint16_t *const r_out[3], float lambda,
+                   float m1, float m2, int64_t nx, int64_t ny, int64_t nz, void *stream);
+
+/*
+ * tv_fgp_run_h with two steps per pass (tv_fgp_step2_h): the steps of each
+ * outer iteration run in pairs, p alternating between p and p_ws, an odd
+ * last step runs tv_fgp_step_h's kernel in place, and if p ends in p_ws it is
+ * copied back into p on the stream.  p_ws: 3*nx*ny*nz binary16 values (three
+ * consecutive volumes), overlapping nothing else.  Results equal
+ * tv_fgp_run_h's bit for bit; r_final names the buffer with the last r.
+ */
+int tv_fgp_run2_h(const float *b, uint16_t *const p[3], uint16_t *p_ws,
+                  uint16_t *const r_a[3], uint16_t *const r_b[3], float lambda, int n_outer,
+                  int n_inner, int64_t nx, int64_t ny, int64_t nz, void *stream,
+                  int *r_final);
+
 /* tv_primal from a binary16 dual: z = max(b - lambda * L(p), 0) in float. */
 int tv_primal_h(const float *b, const uint16_t *const p[3], float *z, float lambda,
                 int64_t nx, int64_t ny, int64_t nz, void *stream);

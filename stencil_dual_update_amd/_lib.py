@@ -36,7 +36,7 @@ VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
 
 # Names declared in include/tv_fgp.h, in declaration order.
 EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_fgp_step2", "tv_primal",
-           "tv_fgp_step_h", "tv_fgp_run_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
+           "tv_fgp_step_h", "tv_fgp_run_h", "tv_fgp_step2_h", "tv_fgp_run2_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
            "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_status_string",
            "tv_fgp_variant_name")
 
@@ -83,6 +83,11 @@ def _load():
     lib.tv_fgp_run_h.restype = ctypes.c_int
     lib.tv_fgp_run_h.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int, I64, I64, I64,
                                  P, ctypes.POINTER(ctypes.c_int)]
+    lib.tv_fgp_step2_h.restype = ctypes.c_int
+    lib.tv_fgp_step2_h.argtypes = [P, P3, P3, P3, P3, F, F, F, I64, I64, I64, P]
+    lib.tv_fgp_run2_h.restype = ctypes.c_int
+    lib.tv_fgp_run2_h.argtypes = [P, P3, P, P3, P3, F, ctypes.c_int, ctypes.c_int, I64, I64, I64,
+                                  P, ctypes.POINTER(ctypes.c_int)]
     lib.tv_primal_h.restype = ctypes.c_int
     lib.tv_primal_h.argtypes = [P, P3, P, F, I64, I64, I64, P]
     lib.tv_fgp_gap_workspace_bytes.restype = ctypes.c_size_t
@@ -366,6 +371,34 @@ def tv_fgp_run_h(b, p, r_a, r_b, lam, n_outer, n_inner, stream=None, dims=None):
                           _hfield(r_b, shape, "r_b"), float(lam), int(n_outer), int(n_inner),
                           nx, ny, nz, _stream(stream), ctypes.byref(where))
     _raise(st, "tv_fgp_run_h")
+    return where.value
+
+
+def tv_fgp_step2_h(b, p_in, p_out, r_in, r_out, lam, m1, m2, stream=None, dims=None):
+    """tv_fgp_step2 with the binary16 dual (float16 or int16 tensors)."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    st = lib.tv_fgp_step2_h(_addr(b), _hfield(p_in, shape, "p_in"),
+                            _hfield(p_out, shape, "p_out"), _hfield(r_in, shape, "r_in"),
+                            _hfield(r_out, shape, "r_out"), float(lam), float(m1), float(m2),
+                            nx, ny, nz, _stream(stream))
+    _raise(st, "tv_fgp_step2_h")
+
+
+def tv_fgp_run2_h(b, p, p_ws, r_a, r_b, lam, n_outer, n_inner, stream=None, dims=None):
+    """tv_fgp_run_h with two steps per pass; p_ws holds three binary16 volumes
+    ((3, nz, ny, nx) tensor).  Returns 0 if the last r is in r_a, 1 if in r_b."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_half(p_ws, (3,) + shape, "p_ws")
+    where = ctypes.c_int(-1)
+    st = lib.tv_fgp_run2_h(_addr(b), _hfield(p, shape, "p"), _addr(p_ws),
+                           _hfield(r_a, shape, "r_a"), _hfield(r_b, shape, "r_b"), float(lam),
+                           int(n_outer), int(n_inner), nx, ny, nz, _stream(stream),
+                           ctypes.byref(where))
+    _raise(st, "tv_fgp_run2_h")
     return where.value
 
 

@@ -445,6 +445,137 @@ int tv_fgp_run_h(const float *b, uint16_t *const p[3], uint16_t *const r_a[3],
   return TV_OK;
 }
 
+int tv_fgp_step2_h(const float *b, const uint16_t *const p_in[3], uint16_t *const p_out[3],
+                   const uint16_t *const r_in[3], uint16_t *const r_out[3], float lambda,
+                   float m1, float m2, int64_t nx, int64_t ny, int64_t nz, void *stream) {
+  if (p_in == nullptr || p_out == nullptr || r_in == nullptr || r_out == nullptr)
+    return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  if (!isfinite(m1) || !isfinite(m2)) return TV_ERR_PARAM;
+  const size_t hb = bytes / 2;
+  const Buf bufs[13] = {vol(b, bytes, false),       hvol(p_in[0], hb, false),
+                        hvol(p_in[1], hb, false),   hvol(p_in[2], hb, false),
+                        hvol(p_out[0], hb, true),   hvol(p_out[1], hb, true),
+                        hvol(p_out[2], hb, true),   hvol(r_in[0], hb, false),
+                        hvol(r_in[1], hb, false),   hvol(r_in[2], hb, false),
+                        hvol(r_out[0], hb, true),   hvol(r_out[1], hb, true),
+                        hvol(r_out[2], hb, true)};
+  st = check_buffers(bufs, 13);
+  if (st != TV_OK) return st;
+  tvfgp::Step2ArgsH a;
+  a.b = b;
+  for (int q = 0; q < 3; ++q) {
+    a.p_in[q] = p_in[q];
+    a.p_out[q] = p_out[q];
+    a.r_in[q] = r_in[q];
+    a.r_out[q] = r_out[q];
+  }
+  a.lam = lambda;
+  a.c = c;
+  a.m1 = m1;
+  a.m2 = m2;
+  a.nx = nx;
+  a.ny = ny;
+  a.nz = nz;
+  a.stream = stream;
+  return launch_status(tvfgp::launch_tb2_h(a));
+}
+
+int tv_fgp_run2_h(const float *b, uint16_t *const p[3], uint16_t *p_ws,
+                  uint16_t *const r_a[3], uint16_t *const r_b[3], float lambda, int n_outer,
+                  int n_inner, int64_t nx, int64_t ny, int64_t nz, void *stream,
+                  int *r_final) {
+  if (r_final) *r_final = 0;
+  if (p == nullptr || r_a == nullptr || r_b == nullptr || p_ws == nullptr)
+    return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  if (n_outer < 0 || n_inner < 0) return TV_ERR_PARAM;
+  const size_t hb = bytes / 2;
+  const Buf bufs[11] = {vol(b, bytes, false),   hvol(p[0], hb, true),
+                        hvol(p[1], hb, true),   hvol(p[2], hb, true),
+                        hvol(r_a[0], hb, true), hvol(r_a[1], hb, true),
+                        hvol(r_a[2], hb, true), hvol(r_b[0], hb, true),
+                        hvol(r_b[1], hb, true), hvol(r_b[2], hb, true),
+                        hvol(p_ws, 3 * hb, true)};
+  st = check_buffers(bufs, 11);
+  if (st != TV_OK) return st;
+  const size_t n = hb / sizeof(uint16_t);
+  uint16_t *const ws[3] = {p_ws, p_ws + n, p_ws + 2 * n};
+  uint16_t *const *cur = p;
+  uint16_t *const *alt = ws;
+  int where = 0;
+  for (int o = 0; o < n_outer; ++o) {
+    double t = 1.0;
+    for (int k = 1; k <= n_inner;) {
+      const int todo = n_inner - k + 1 >= 2 ? 2 : 1;
+      float m[2];
+      for (int q = 0; q < todo; ++q) {
+        const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
+        m[q] = (float)((t - 1.0) / t_next);
+        t = t_next;
+      }
+      uint16_t *const *in = where ? r_b : r_a;
+      uint16_t *const *out = where ? r_a : r_b;
+      if (todo == 2) {
+        tvfgp::Step2ArgsH a;
+        a.b = b;
+        for (int q = 0; q < 3; ++q) {
+          a.p_in[q] = cur[q];
+          a.p_out[q] = alt[q];
+          a.r_in[q] = in[q];
+          a.r_out[q] = out[q];
+        }
+        a.lam = lambda;
+        a.c = c;
+        a.m1 = m[0];
+        a.m2 = m[1];
+        a.nx = nx;
+        a.ny = ny;
+        a.nz = nz;
+        a.stream = stream;
+        if (tvfgp::launch_tb2_h(a) != 0) return TV_ERR_LAUNCH;
+        uint16_t *const *tmp = cur;
+        cur = alt;
+        alt = tmp;
+      } else {
+        tvfgp::StepArgsH h;
+        h.b = b;
+        for (int q = 0; q < 3; ++q) {
+          h.p[q] = cur[q];
+          h.r_in[q] = in[q];
+          h.r_out[q] = out[q];
+        }
+        h.lam = lambda;
+        h.c = c;
+        h.m = m[0];
+        h.nx = nx;
+        h.ny = ny;
+        h.nz = nz;
+        h.stream = stream;
+        if (tvfgp::launch_fused_pair_h(h) != 0) return TV_ERR_LAUNCH;
+      }
+      where ^= 1;
+      if (r_final) *r_final = where;
+      k += todo;
+    }
+  }
+  if (cur != p) {
+    for (int q = 0; q < 3; ++q)
+      if (hipMemcpyAsync(p[q], cur[q], hb, hipMemcpyDeviceToDevice, (hipStream_t)stream) !=
+          hipSuccess)
+        return TV_ERR_LAUNCH;
+  }
+  return TV_OK;
+}
+
 int tv_primal_h(const float *b, const uint16_t *const p[3], float *z, float lambda,
                 int64_t nx, int64_t ny, int64_t nz, void *stream) {
   if (p == nullptr) return TV_ERR_NULL;

@@ -56,6 +56,18 @@ struct Step2Args {
   void *stream;
 };
 
+// Step2Args with the dual stored as binary16.
+struct Step2ArgsH {
+  const float *b;
+  const uint16_t *p_in[3];
+  uint16_t *p_out[3];
+  const uint16_t *r_in[3];
+  uint16_t *r_out[3];
+  float lam, c, m1, m2;
+  int64_t nx, ny, nz;
+  void *stream;
+};
+
 struct PrimalArgs {
   const float *b;
   const float *p[3];
@@ -109,6 +121,7 @@ int launch_fused_zx_h(const StepArgsH &a);
 int launch_fused_pair(const StepArgs &a);
 int launch_fused_pair_h(const StepArgsH &a);
 int launch_tb2(const Step2Args &a);
+int launch_tb2_h(const Step2ArgsH &a);
 // Cube-tiled ablation, shape chosen by a.variant (kVariantCube...).
 int launch_cube(const StepArgs &a);
 int launch_primal_h(const PrimalArgsH &a);

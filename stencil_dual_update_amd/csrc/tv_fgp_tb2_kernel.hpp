@@ -114,21 +114,29 @@ __device__ __forceinline__ void tb_init_point(TbPoint<Off> &pt, int lx, int ly, 
 
 // Loads of plane kp into the "next" registers (caller checks 0 <= kp < nz).
 // A point outside the volume has offset 0 and loads the plane's first voxel,
-// which is in bounds; its values are never used.
-template <typename Off>
+// which is in bounds; its values are never used.  S is the element type of
+// the dual volumes (float, or _Float16: widened exactly).
+template <typename S, typename Off>
 __device__ __forceinline__ void tb_load(TbPoint<Off> &pt, Off kp_off, Off sy4,
                                         const float *__restrict__ b,
-                                        const float *__restrict__ r0,
-                                        const float *__restrict__ r1,
-                                        const float *__restrict__ r2) {
+                                        const S *__restrict__ r0,
+                                        const S *__restrict__ r1,
+                                        const S *__restrict__ r2) {
   const Off four = 4;
   const Off j = pt.o + kp_off;
   pt.nb = ld(b, j);
-  pt.n0 = ld(r0, j);
-  pt.n1 = ld(r1, j);
-  pt.n2 = ld(r2, j);
-  pt.n0l = ld(r0, pt.low_x ? j - four : j);
-  pt.n1l = ld(r1, pt.low_y ? j - sy4 : j);
+  pt.n0 = lds(r0, j);
+  pt.n1 = lds(r1, j);
+  pt.n2 = lds(r2, j);
+  pt.n0l = lds(r0, pt.low_x ? j - four : j);
+  pt.n1l = lds(r1, pt.low_y ? j - sy4 : j);
+}
+
+// A value as it reads back after a store to an S volume (identity for float;
+// for _Float16 the round to nearest, ties to even, widened again exactly).
+template <typename S>
+__device__ __forceinline__ float as_stored(float v) {
+  return (float)(S)v;
 }
 
 template <typename Off>
@@ -159,14 +167,16 @@ __device__ __forceinline__ void tb_rotate(TbPoint<Off> &pt) {
 // Six waves per SIMD (three workgroups per CU) measured ~9% faster than the
 // five the unconstrained register allocation allows; the cap costs a couple
 // of spilled registers.
-template <typename I, typename Off>
+// S: element type of p and r (float, or _Float16 for the binary16 dual, where
+// the first step's p' and r' are rounded to binary16 as a stored step's are).
+template <typename I, typename Off, typename S>
 __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
-    const float *__restrict__ b, const float *__restrict__ pi0,
-    const float *__restrict__ pi1, const float *__restrict__ pi2,
-    float *__restrict__ po0, float *__restrict__ po1, float *__restrict__ po2,
-    const float *__restrict__ ri0, const float *__restrict__ ri1,
-    const float *__restrict__ ri2, float *__restrict__ ro0, float *__restrict__ ro1,
-    float *__restrict__ ro2, float lam, float c, float m1, float m2,
+    const float *__restrict__ b, const S *__restrict__ pi0,
+    const S *__restrict__ pi1, const S *__restrict__ pi2,
+    S *__restrict__ po0, S *__restrict__ po1, S *__restrict__ po2,
+    const S *__restrict__ ri0, const S *__restrict__ ri1,
+    const S *__restrict__ ri2, S *__restrict__ ro0, S *__restrict__ ro1,
+    S *__restrict__ ro2, float lam, float c, float m1, float m2,
     ZxGeometry<I, Off> g) {
   __shared__ float z0r[2][kTbR0Y][kTbR0X];    // z0 at (x+1, y+1)
   __shared__ float rxs[kTbE1Y][kTbE1X];       // r'_x at (x+1, y+1)
@@ -201,12 +211,12 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
     // and the inputs of plane z0 - 1 as "current"
     if (z0 - 2 >= 0) {
       const Off j = (Off)(z0 - 2) * sz4;
-      own.q2 = ld(ri2, own.o + j);
-      if (has_halo) hal.q2 = ld(ri2, hal.o + j);
+      own.q2 = lds(ri2, own.o + j);
+      if (has_halo) hal.q2 = lds(ri2, hal.o + j);
     }
     if (input_plane(z0 - 1)) {
-      tb_load(own, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
-      if (has_halo) tb_load(hal, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
+      tb_load<S, Off>(own, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
+      if (has_halo) tb_load<S, Off>(hal, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
     }
     tb_take(own);
     tb_take(hal);
@@ -222,20 +232,20 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
       // p_in of the step-one plane
       if (do_d) {
         const Off j = (Off)kd * sz4;
-        own.pp0 = ld(pi0, own.o + j);
-        own.pp1 = ld(pi1, own.o + j);
-        own.pp2 = ld(pi2, own.o + j);
+        own.pp0 = lds(pi0, own.o + j);
+        own.pp1 = lds(pi1, own.o + j);
+        own.pp2 = lds(pi2, own.o + j);
         if (has_halo) {
-          hal.pp0 = ld(pi0, hal.o + j);
-          hal.pp1 = ld(pi1, hal.o + j);
-          hal.pp2 = ld(pi2, hal.o + j);
+          hal.pp0 = lds(pi0, hal.o + j);
+          hal.pp1 = lds(pi1, hal.o + j);
+          hal.pp2 = lds(pi2, hal.o + j);
         }
       }
       // inputs of plane k+4, consumed next iteration
       const I kl = k + 4;
       if (input_plane(kl)) {
-        tb_load(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
-        if (has_halo) tb_load(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+        tb_load<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+        if (has_halo) tb_load<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
       }
 
       // ---- phase 1: z1 of plane k+1 on R1, z0 of plane k+3 on R0
@@ -276,12 +286,12 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
         dual_update(zi, zx, zy, zz, own.has_x, own.has_y, k + 1 < g.nz, ra0, ra1, ra2,
                     pa0, pa1, pa2, c, m2, o0, o1, o2);
         const Off j = own.o + (Off)k * sz4;
-        st_stream(po0, j, pa0);
-        st_stream(po1, j, pa1);
-        st_stream(po2, j, pa2);
-        st_stream(ro0, j, o0);
-        st_stream(ro1, j, o1);
-        st_stream(ro2, j, o2);
+        sts_stream(po0, j, pa0);
+        sts_stream(po1, j, pa1);
+        sts_stream(po2, j, pa2);
+        sts_stream(ro0, j, o0);
+        sts_stream(ro1, j, o1);
+        sts_stream(ro2, j, o2);
       }
       pa0 = pb0;
       pa1 = pb1;
@@ -296,6 +306,13 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
         const float zz = z0r[sn][y][x];
         dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd + 1 < g.nz, pt.q0, pt.q1, pt.q2,
                     pt.pp0, pt.pp1, pt.pp2, c, m1, r0o, r1o, r2o);
+        // the second step sees the first step's p' and r' as stored
+        pt.pp0 = as_stored<S>(pt.pp0);
+        pt.pp1 = as_stored<S>(pt.pp1);
+        pt.pp2 = as_stored<S>(pt.pp2);
+        r0o = as_stored<S>(r0o);
+        r1o = as_stored<S>(r1o);
+        r2o = as_stored<S>(r2o);
         rxs[y][x] = r0o;
         rys[y][x] = r1o;
         rzs[s][y][x] = r2o;

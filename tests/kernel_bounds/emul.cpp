@@ -11,7 +11,7 @@
 // usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
 //   variant: fused | fused_nostream | fused_h | fused_nostream_h | pair | pair_nostream |
 //            pair_h | pair_nostream_h | reg_march | point | two_kernel | lds_march |
-//            primal | primal_h | gap | tb2 | cube | cube_32x8x2 | cube_64x8x1 |
+//            primal | primal_h | gap | tb2 | tb2_h | cube | cube_32x8x2 | cube_64x8x1 |
 //            cube_8x8x8 | cube_32x4x4
 //   (the pair variants need an even nx; with an odd one they report "ok" without running)
 //   wide: 1 instantiates the 64-bit offset / index path regardless of size
@@ -83,13 +83,19 @@ struct Bufs {
   float *b, *p[3], *ri[3], *ro[3], *z, *po[3];
 };
 
-template <typename I, typename Off>
+template <typename I, typename Off, typename S>
 void run_tb2(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid, int64_t planes) {
   const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz, planes);
+  S *p[3], *po[3], *ri[3], *ro[3];
+  for (int a = 0; a < 3; ++a) {
+    p[a] = (S *)v.p[a];
+    po[a] = (S *)v.po[a];
+    ri[a] = (S *)v.ri[a];
+    ro[a] = (S *)v.ro[a];
+  }
   run_grid(pick_grid(g.ntiles, grid), tvfgp::kTbBlock, [&] {
-    tvfgp::tb2_kernel<I, Off>(v.b, v.p[0], v.p[1], v.p[2], v.po[0], v.po[1], v.po[2], v.ri[0],
-                              v.ri[1], v.ri[2], v.ro[0], v.ro[1], v.ro[2], 0.01f, 8.3f, 0.3f,
-                              0.5f, g);
+    tvfgp::tb2_kernel<I, Off, S>(v.b, p[0], p[1], p[2], po[0], po[1], po[2], ri[0], ri[1], ri[2],
+                                 ro[0], ro[1], ro[2], 0.01f, 8.3f, 0.3f, 0.5f, g);
   });
 }
 
@@ -245,11 +251,18 @@ int main(int argc, char **argv) {
       run_fused<int64_t, uint64_t, float>(v, nx, ny, nz, grid, sp);
     else
       run_fused<int32_t, uint32_t, float>(v, nx, ny, nz, grid, sp);
-  } else if (!strcmp(variant, "tb2")) {
-    if (wide)
-      run_tb2<int64_t, uint64_t>(v, nx, ny, nz, grid, planes);
-    else
-      run_tb2<int32_t, uint32_t>(v, nx, ny, nz, grid, planes);
+  } else if (!strcmp(variant, "tb2") || !strcmp(variant, "tb2_h")) {
+    if (half) {
+      if (wide)
+        run_tb2<int64_t, uint64_t, _Float16>(v, nx, ny, nz, grid, planes);
+      else
+        run_tb2<int32_t, uint32_t, _Float16>(v, nx, ny, nz, grid, planes);
+    } else {
+      if (wide)
+        run_tb2<int64_t, uint64_t, float>(v, nx, ny, nz, grid, planes);
+      else
+        run_tb2<int32_t, uint32_t, float>(v, nx, ny, nz, grid, planes);
+    }
   } else if (!strncmp(variant, "pair", 4)) {
     const bool sp = strstr(variant, "nostream") == nullptr;
     if (nx % 2 != 0) {

@@ -14,6 +14,8 @@
 //           lds_march  one step (m1) with the LDS z-march (8 planes per tile)
 //           gap    duality gap of p (three doubles written to <dir>/gap.bin)
 //           tb2    two steps (m1 then m2) in one pass, p_in -> p_out
+//           tb2_h  the same with p and r stored as binary16 (files hold the
+//                  binary16 values as floats)
 //   dir holds b.bin (n floats), p.bin and r.bin (3n floats each); the kernel
 //   writes p_out.bin and r_out.bin there.
 #include <condition_variable>
@@ -158,10 +160,28 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
   } else if (!strcmp(kernel, "tb2")) {
     const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz, planes);
     run_grid(pick(g.ntiles, grid), tvfgp::kTbBlock, [&] {
-      tvfgp::tb2_kernel<I, Off>(b, p, p + n, p + 2 * n, p_out, p_out + n, p_out + 2 * n, r,
-                                r + n, r + 2 * n, r_out, r_out + n, r_out + 2 * n, lam, c, m1,
-                                m2, g);
+      tvfgp::tb2_kernel<I, Off, float>(b, p, p + n, p + 2 * n, p_out, p_out + n, p_out + 2 * n,
+                                       r, r + n, r + 2 * n, r_out, r_out + n, r_out + 2 * n, lam,
+                                       c, m1, m2, g);
     });
+  } else if (!strcmp(kernel, "tb2_h")) {
+    // binary16 dual: the inputs must be binary16 values (converted exactly)
+    typedef _Float16 h;
+    std::vector<h> ph(3 * n), rh(3 * n), poh(3 * n), roh(3 * n);
+    for (size_t i = 0; i < 3 * n; ++i) {
+      ph[i] = (h)p[i];
+      rh[i] = (h)r[i];
+    }
+    const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz, planes);
+    h *P = ph.data(), *R = rh.data(), *PO = poh.data(), *RO = roh.data();
+    run_grid(pick(g.ntiles, grid), tvfgp::kTbBlock, [&] {
+      tvfgp::tb2_kernel<I, Off, h>(b, P, P + n, P + 2 * n, PO, PO + n, PO + 2 * n, R, R + n,
+                                   R + 2 * n, RO, RO + n, RO + 2 * n, lam, c, m1, m2, g);
+    });
+    for (size_t i = 0; i < 3 * n; ++i) {
+      p_out[i] = (float)poh[i];
+      r_out[i] = (float)roh[i];
+    }
   } else {
     fprintf(stderr, "unknown kernel %s\n", kernel);
     exit(2);

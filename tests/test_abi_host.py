@@ -350,3 +350,39 @@ def step2(b=0, pi=(1, 2, 3), po=(10, 11, 12), ri=(4, 5, 6), ro=(7, 8, 9), lam=0.
 ])
 def test_step2_rejects(kw, code):
     assert step2(**kw) == code
+
+
+def step2_h(b=0, pi=(1, 2, 3), po=(10, 11, 12), ri=(4, 5, 6), ro=(7, 8, 9), lam=0.01, m1=0.0,
+            m2=0.3, dims=(NX, NY, NZ)):
+    return L.tv_fgp_step2_h(None if b is None else addr(b), field(*pi), field(*po), field(*ri),
+                            field(*ro), lam, m1, m2, *dims, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=None), tvf.TV_ERR_NULL),
+    (dict(dims=(0, NY, NZ)), tvf.TV_ERR_DIMS),
+    (dict(m2=float("nan")), tvf.TV_ERR_PARAM),
+    (dict(po=(1, 11, 12)), tvf.TV_ERR_ALIAS),
+    (dict(ro=(7, 8, 0)), tvf.TV_ERR_ALIAS),
+])
+def test_step2_h_rejects(kw, code):
+    assert step2_h(**kw) == code
+
+
+def run2_h(ws, n_outer=0, b=0):
+    where = ctypes.c_int(-7)
+    st = L.tv_fgp_run2_h(addr(b), field(1, 2, 3), ws, field(4, 5, 6), field(7, 8, 9), 0.01,
+                         n_outer, 3, NX, NY, NZ, None, ctypes.byref(where))
+    return st, where.value
+
+
+def test_run2_h_workspace():
+    # three binary16 volumes: 3 * VOL / 2 bytes from ws; nothing enqueued with n_outer = 0
+    assert run2_h(None)[0] == tvf.TV_ERR_NULL
+    assert run2_h(addr(10)) == (tvf.TV_OK, 0)
+    ws = addr(10)
+    assert run2_h(ws, b=0)[0] == tvf.TV_OK
+    assert L.tv_fgp_run2_h(ws + 3 * VOL // 2 - 4, field(1, 2, 3), ws, field(4, 5, 6),
+                           field(7, 8, 9), 0.01, 0, 3, NX, NY, NZ, None, None) == tvf.TV_ERR_ALIAS
+    assert run2_h(addr(9))[0] == tvf.TV_ERR_ALIAS   # first volume is r_b[2]
+    assert run2_h(addr(10) + 1)[0] == tvf.TV_ERR_ALIGN

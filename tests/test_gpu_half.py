@@ -194,3 +194,50 @@ def test_half_nan_guard_bands(tvf, dims, guard):
     assert nan(host[:, :guard]).all() and nan(host[:, guard + n:]).all()
     assert_bits_equal(np.stack([to_host_bits(t) for t in p]), pe, "p")
     assert_bits_equal(np.stack([to_host_bits(t) for t in r]), re, "r")
+
+
+def gpu_run2_half(tvf, b, p_bits, r_bits, lam, n_outer, n_inner):
+    bt = torch.from_numpy(np.ascontiguousarray(b)).to("cuda")
+    p = to_dev_half(p_bits)
+    ra = to_dev_half(r_bits)
+    rb = torch.empty_like(ra)
+    ws = torch.empty_like(p)
+    where = tvf.tv_fgp_run2_h(bt, p, ws, ra, rb, lam, n_outer, n_inner)
+    torch.cuda.synchronize()
+    return to_host_bits(p), to_host_bits(rb if where else ra)
+
+
+@pytest.mark.parametrize("dims,n_outer,n_inner", [
+    ((67, 45, 29), 2, 5), ((130, 17, 40), 1, 4), ((64, 8, 70), 1, 3), ((1, 1, 1), 1, 2),
+    ((5, 70, 3), 3, 2), ((1000, 7, 3), 1, 6)], ids=lambda c: str(c))
+def test_run2_half_matches_oracle(tvf, dims, n_outer, n_inner):
+    """Two binary16 steps per pass against the oracle's half mode, odd and even inner counts."""
+    b, p0, r0 = half_inputs(4, dims)
+    pe, re = oracle.run_half(b, p0, r0, 0.003, n_outer, n_inner)
+    pg, rg = gpu_run2_half(tvf, b, p0, r0, 0.003, n_outer, n_inner)
+    assert_bits_equal(pg, pe, "p %s" % (dims,))
+    assert_bits_equal(rg, re, "r %s" % (dims,))
+
+
+def test_step2_half_equals_two_half_steps(tvf):
+    b, p0, r0 = half_inputs(4, (70, 33, 19))
+    m1, m2 = float(np.float32(oracle.momentum(3))), float(np.float32(oracle.momentum(4)))
+    p2, r2 = oracle.run_half(b, p0, r0, 0.003, 1, 2)      # state after steps 1, 2
+    pe, re = oracle.run_half(b, p0, r0, 0.003, 1, 4)      # then steps 3, 4
+    bt = torch.from_numpy(b).to("cuda")
+    pi, ri = to_dev_half(p2), to_dev_half(r2)
+    po, ro = torch.empty_like(pi), torch.empty_like(ri)
+    tvf.tv_fgp_step2_h(bt, pi, po, ri, ro, 0.003, m1, m2)
+    torch.cuda.synchronize()
+    assert_bits_equal(to_host_bits(po), pe, "p")
+    assert_bits_equal(to_host_bits(ro), re, "r")
+    assert np.array_equal(to_host_bits(pi), p2)
+
+
+def test_run2_half_workload1_full(tvf):
+    w = phantoms.workload(1)
+    b, p0, r0 = half_inputs(1)
+    pe, re = oracle.run_half(b, p0, r0, w["lam"], 2, 10)
+    pg, rg = gpu_run2_half(tvf, b, p0, r0, w["lam"], 2, 10)
+    assert_bits_equal(pg, pe, "p")
+    assert_bits_equal(rg, re, "r")

@@ -126,3 +126,17 @@ def test_two_steps_per_pass(func, tmp_path, dims, wide, grid, planes):
     pe, re = oracle.step(b, pe, re, 0.003, m2)
     assert_bits(pg, pe, "p %s" % (dims,))
     assert_bits(rg, re, "r %s" % (dims,))
+
+
+@pytest.mark.parametrize("dims,planes", [((65, 9, 17), 0), ((64, 8, 48), 16), ((5, 70, 3), 0)],
+                         ids=lambda c: str(c))
+def test_two_steps_per_pass_binary16(func, tmp_path, dims, planes):
+    """The binary16 two-step pass equals two steps of the oracle's half mode."""
+    b, p0, r0 = inputs(dims)
+    ph, rh = oracle.f32_to_f16_bits(p0), oracle.f32_to_f16_bits(r0)
+    pg, rg = emulate(func, tmp_path, "tb2_h", b, oracle.f16_bits_to_f32(ph),
+                     oracle.f16_bits_to_f32(rh), 0.003, np.float32(oracle.momentum(1)),
+                     np.float32(oracle.momentum(2)), 0, 0, planes)
+    pe, re = oracle.run_half(b, ph, rh, 0.003, 1, 2)
+    assert np.array_equal(oracle.f32_to_f16_bits(pg), pe)
+    assert np.array_equal(oracle.f32_to_f16_bits(rg), re)
