@@ -31,7 +31,8 @@ Besides the headline ms/step it reports:
 
 --storage half runs the step with p and r stored as binary16 (fp32
 arithmetic; 28 B per voxel: read b, r (3), p (3) at 4 + 6 + 6 B, write p (3),
-r (3) at 6 + 6 B); its CPU baseline is the oracle's half mode.
+r (3) at 6 + 6 B), by default two steps per pass (tv_fgp_run2_h; --variant
+fused for one step per pass); its CPU baseline is the oracle's half mode.
 """
 import argparse
 import hashlib
