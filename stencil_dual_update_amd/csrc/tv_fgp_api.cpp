@@ -93,57 +93,41 @@ tvfgp::StepArgs make_step(const float *b, float *const p[3],
 
 int launch_status(int rc) { return rc == 0 ? TV_OK : TV_ERR_LAUNCH; }
 
-// Inner loop of the two-steps-per-pass variant: steps are launched in pairs
-// (one pass each, p alternating between the caller's p and the workspace
-// p_ws), an odd last step of an outer iteration runs the fused kernel in
-// place, and if p ends in the workspace it is copied back.
-int enqueue_steps_tb2(const float *b, float *const p[3], float *const r_a[3],
-                      float *const r_b[3], float lambda, float c, int n_outer,
-                      int n_inner, int64_t nx, int64_t ny, int64_t nz,
-                      float *p_ws, size_t bytes, void *stream, int *where) {
-  const size_t n = bytes / sizeof(float);
-  float *const ws[3] = {p_ws, p_ws + n, p_ws + 2 * n};
-  float *const *cur = p;
-  float *const *alt = ws;
+// Inner loop of the two-steps-per-pass kernels, for fp32 (T = float) and
+// binary16 (T = uint16_t) duals: the steps of each outer iteration run in
+// pairs, one pass(p_in, p_out, r_in, r_out, m_k, m_k+1) each, p alternating
+// between the caller's p and the workspace p_ws; an odd last step of an outer
+// iteration runs single(p, r_in, r_out, m) in place; if p ends in the
+// workspace it is copied back.  `where` (0: r_a holds r, 1: r_b) flips after
+// every launch.  pass and single return 0 on success.
+template <typename T, typename Pass, typename Single>
+int enqueue_pairs(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], int n_outer,
+                  int n_inner, size_t vol_bytes, void *stream, int *where, Pass pass,
+                  Single single) {
+  const size_t n = vol_bytes / sizeof(T);
+  T *const ws[3] = {p_ws, p_ws + n, p_ws + 2 * n};
+  T *const *cur = p;
+  T *const *alt = ws;
   for (int o = 0; o < n_outer; ++o) {
     double t = 1.0;
     for (int k = 1; k <= n_inner;) {
       const int todo = n_inner - k + 1 >= 2 ? 2 : 1;
-      float m[2];
+      float m[2] = {0.0f, 0.0f};
       // m_k and m_{k+1}, evaluated as in the one-step loop
       for (int s = 0; s < todo; ++s) {
         const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
         m[s] = (float)((t - 1.0) / t_next);
         t = t_next;
       }
-      float *const *in = *where ? r_b : r_a;
-      float *const *out = *where ? r_a : r_b;
+      T *const *in = *where ? r_b : r_a;
+      T *const *out = *where ? r_a : r_b;
       if (todo == 2) {
-        tvfgp::Step2Args a;
-        a.b = b;
-        for (int q = 0; q < 3; ++q) {
-          a.p_in[q] = cur[q];
-          a.p_out[q] = alt[q];
-          a.r_in[q] = in[q];
-          a.r_out[q] = out[q];
-        }
-        a.lam = lambda;
-        a.c = c;
-        a.m1 = m[0];
-        a.m2 = m[1];
-        a.nx = nx;
-        a.ny = ny;
-        a.nz = nz;
-        a.stream = stream;
-        if (tvfgp::launch_tb2(a) != 0) return TV_ERR_LAUNCH;
-        float *const *tmp = cur;
+        if (pass(cur, alt, in, out, m[0], m[1]) != 0) return TV_ERR_LAUNCH;
+        T *const *tmp = cur;
         cur = alt;
         alt = tmp;
-      } else {
-        const float *cin[3] = {in[0], in[1], in[2]};
-        if (tvfgp::launch_step(make_step(b, cur, cin, out, lambda, c, m[0], nx, ny, nz,
-                                         tvfgp::kVariantFused, nullptr, stream)) != 0)
-          return TV_ERR_LAUNCH;
+      } else if (single(cur, in, out, m[0]) != 0) {
+        return TV_ERR_LAUNCH;
       }
       *where ^= 1;
       k += todo;
@@ -151,11 +135,44 @@ int enqueue_steps_tb2(const float *b, float *const p[3], float *const r_a[3],
   }
   if (cur != p) {
     for (int q = 0; q < 3; ++q)
-      if (hipMemcpyAsync(p[q], cur[q], bytes, hipMemcpyDeviceToDevice,
+      if (hipMemcpyAsync(p[q], cur[q], vol_bytes, hipMemcpyDeviceToDevice,
                          (hipStream_t)stream) != hipSuccess)
         return TV_ERR_LAUNCH;
   }
   return TV_OK;
+}
+
+int enqueue_steps_tb2(const float *b, float *const p[3], float *const r_a[3],
+                      float *const r_b[3], float lambda, float c, int n_outer,
+                      int n_inner, int64_t nx, int64_t ny, int64_t nz,
+                      float *p_ws, size_t bytes, void *stream, int *where) {
+  auto pass = [&](float *const *pi, float *const *po, float *const *ri, float *const *ro,
+                  float m1, float m2) {
+    tvfgp::Step2Args a;
+    a.b = b;
+    for (int q = 0; q < 3; ++q) {
+      a.p_in[q] = pi[q];
+      a.p_out[q] = po[q];
+      a.r_in[q] = ri[q];
+      a.r_out[q] = ro[q];
+    }
+    a.lam = lambda;
+    a.c = c;
+    a.m1 = m1;
+    a.m2 = m2;
+    a.nx = nx;
+    a.ny = ny;
+    a.nz = nz;
+    a.stream = stream;
+    return tvfgp::launch_tb2(a);
+  };
+  auto single = [&](float *const *pc, float *const *ri, float *const *ro, float m) {
+    const float *cin[3] = {ri[0], ri[1], ri[2]};
+    return tvfgp::launch_step(make_step(b, pc, cin, ro, lambda, c, m, nx, ny, nz,
+                                        tvfgp::kVariantFused, nullptr, stream));
+  };
+  return enqueue_pairs<float>(p, p_ws, r_a, r_b, n_outer, n_inner, bytes, stream, where, pass,
+                              single);
 }
 
 // Enqueue n_outer x n_inner steps; `where` (0: r_a holds r, 1: r_b) is
@@ -507,73 +524,48 @@ int tv_fgp_run2_h(const float *b, uint16_t *const p[3], uint16_t *p_ws,
                         hvol(p_ws, 3 * hb, true)};
   st = check_buffers(bufs, 11);
   if (st != TV_OK) return st;
-  const size_t n = hb / sizeof(uint16_t);
-  uint16_t *const ws[3] = {p_ws, p_ws + n, p_ws + 2 * n};
-  uint16_t *const *cur = p;
-  uint16_t *const *alt = ws;
-  int where = 0;
-  for (int o = 0; o < n_outer; ++o) {
-    double t = 1.0;
-    for (int k = 1; k <= n_inner;) {
-      const int todo = n_inner - k + 1 >= 2 ? 2 : 1;
-      float m[2];
-      for (int q = 0; q < todo; ++q) {
-        const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
-        m[q] = (float)((t - 1.0) / t_next);
-        t = t_next;
-      }
-      uint16_t *const *in = where ? r_b : r_a;
-      uint16_t *const *out = where ? r_a : r_b;
-      if (todo == 2) {
-        tvfgp::Step2ArgsH a;
-        a.b = b;
-        for (int q = 0; q < 3; ++q) {
-          a.p_in[q] = cur[q];
-          a.p_out[q] = alt[q];
-          a.r_in[q] = in[q];
-          a.r_out[q] = out[q];
-        }
-        a.lam = lambda;
-        a.c = c;
-        a.m1 = m[0];
-        a.m2 = m[1];
-        a.nx = nx;
-        a.ny = ny;
-        a.nz = nz;
-        a.stream = stream;
-        if (tvfgp::launch_tb2_h(a) != 0) return TV_ERR_LAUNCH;
-        uint16_t *const *tmp = cur;
-        cur = alt;
-        alt = tmp;
-      } else {
-        tvfgp::StepArgsH h;
-        h.b = b;
-        for (int q = 0; q < 3; ++q) {
-          h.p[q] = cur[q];
-          h.r_in[q] = in[q];
-          h.r_out[q] = out[q];
-        }
-        h.lam = lambda;
-        h.c = c;
-        h.m = m[0];
-        h.nx = nx;
-        h.ny = ny;
-        h.nz = nz;
-        h.stream = stream;
-        if (tvfgp::launch_fused_pair_h(h) != 0) return TV_ERR_LAUNCH;
-      }
-      where ^= 1;
-      if (r_final) *r_final = where;
-      k += todo;
+  auto pass = [&](uint16_t *const *pi, uint16_t *const *po, uint16_t *const *ri,
+                  uint16_t *const *ro, float m1, float m2) {
+    tvfgp::Step2ArgsH a;
+    a.b = b;
+    for (int q = 0; q < 3; ++q) {
+      a.p_in[q] = pi[q];
+      a.p_out[q] = po[q];
+      a.r_in[q] = ri[q];
+      a.r_out[q] = ro[q];
     }
-  }
-  if (cur != p) {
-    for (int q = 0; q < 3; ++q)
-      if (hipMemcpyAsync(p[q], cur[q], hb, hipMemcpyDeviceToDevice, (hipStream_t)stream) !=
-          hipSuccess)
-        return TV_ERR_LAUNCH;
-  }
-  return TV_OK;
+    a.lam = lambda;
+    a.c = c;
+    a.m1 = m1;
+    a.m2 = m2;
+    a.nx = nx;
+    a.ny = ny;
+    a.nz = nz;
+    a.stream = stream;
+    return tvfgp::launch_tb2_h(a);
+  };
+  auto single = [&](uint16_t *const *pc, uint16_t *const *ri, uint16_t *const *ro, float m) {
+    tvfgp::StepArgsH h;
+    h.b = b;
+    for (int q = 0; q < 3; ++q) {
+      h.p[q] = pc[q];
+      h.r_in[q] = ri[q];
+      h.r_out[q] = ro[q];
+    }
+    h.lam = lambda;
+    h.c = c;
+    h.m = m;
+    h.nx = nx;
+    h.ny = ny;
+    h.nz = nz;
+    h.stream = stream;
+    return tvfgp::launch_fused_pair_h(h);
+  };
+  int where = 0;
+  st = enqueue_pairs<uint16_t>(p, p_ws, r_a, r_b, n_outer, n_inner, hb, stream, &where, pass,
+                               single);
+  if (r_final) *r_final = where;
+  return st;
 }
 
 int tv_primal_h(const float *b, const uint16_t *const p[3], float *z, float lambda,
