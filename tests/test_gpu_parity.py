@@ -359,7 +359,8 @@ def test_workload4_anisotropic_sampled(tvf):
     After K steps a voxel depends only on inputs within K voxels of it, so
     the oracle computes sampled voxels from sub-boxes of the inputs.  After
     200 steps: the corner samples against the oracle, and the properties that
-    hold at every voxel (finite, |p| <= 1, upper-face slots zero).
+    hold at every voxel (finite, |p| <= 1, upper-face slots zero); and the
+    two-steps-per-pass run equal to it at every voxel.
     """
     dims = (1000, 777, 301)
     nx, ny, nz = dims
@@ -388,3 +389,7 @@ def test_workload4_anisotropic_sampled(tvf):
     assert not p[0, :, :, nx - 1].any() and not p[1, :, ny - 1, :].any()
     assert not p[2, nz - 1].any()
     assert (z >= 0).all()
+    # the two-steps-per-pass run gives the same bits at every voxel
+    p2, r2, z2 = gpu_solve(tvf, b, p0, r0, lam, w["n_outer"], w["n_inner"], "tb2")
+    for name, g, e in (("p", p2, p), ("r", r2, r), ("z", z2, z)):
+        assert np.array_equal(g.view(np.uint32), e.view(np.uint32)), "tb2 vs fused " + name
