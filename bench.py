@@ -318,7 +318,10 @@ def main():
         torch.cuda.synchronize()
     gap_ms = g0.elapsed_time(g1) / gap_reps
     gap_vals = gap_out.cpu().tolist()
-    gap = {"ms": round(gap_ms, 5), "algorithmic_bytes": 16 * nvox,
+    # the two-voxels-per-lane first pass takes even nx (torch allocations are
+    # aligned); odd nx takes the one-voxel pass
+    gap = {"first_pass": "gap_partial_pair_kernel" if nx % 2 == 0 else "gap_partial_kernel",
+           "ms": round(gap_ms, 5), "algorithmic_bytes": 16 * nvox,
            "gbps": round(16 * nvox / (gap_ms * 1e-3) / 1e9, 1),
            "frac_of_hbm_peak": round(16 * nvox / (gap_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
            "gap": gap_vals[0], "tv": gap_vals[1], "fidelity": gap_vals[2]}

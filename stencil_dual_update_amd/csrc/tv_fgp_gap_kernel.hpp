@@ -18,6 +18,13 @@
 // z(i+e_y) read from LDS.  The reduction is deterministic: a fixed number of
 // workgroups each sum a fixed set of tiles in a fixed order into one partial
 // triple, and a single workgroup adds the partials in a fixed order.
+//
+// When nx is even and b, p are aligned to two elements, gap_partial_pair_kernel
+// does the first pass instead: two x-adjacent voxels per lane, 128 x 8 tiles
+// of 24 planes, every load a pair, loads issued two planes ahead.  The
+// reduction reads only b and p (16 bytes per voxel), so with one element per
+// load and one plane of prefetch a wave has too few bytes in flight to cover
+// HBM latency; pairs double them and the deeper prefetch doubles them again.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -26,12 +33,18 @@
 
 #include "tv_fgp_device.hpp"
 #include "tv_fgp_fused_kernel.hpp"
+#include "tv_fgp_pair_kernel.hpp"
 
 #pragma clang fp contract(off)
 
 namespace tvfgp {
 
 constexpr int kGapGrid = 1024;    // partial triples (upper bound)
+constexpr int kGapPairGrid = 1024;  // the same for the pair kernel (<= kGapGrid)
+// Planes per tile of the pair kernel: a multiple of 2 (load sets) and of 3
+// (ring slots).  The prefetch drains at each tile's end, so long tiles pay
+// off: at 512^3, 6 / 12 / 24 planes measured 0.58 / 0.50 / 0.47 ms.
+constexpr int kGapPairPlanes = 24;
 constexpr int kGapFinalBlock = 256;
 
 // Per-voxel contribution: |g|, |g| - g.p and 1/2 (z - b)^2, in fp64.
@@ -210,6 +223,172 @@ __global__ __launch_bounds__(kZxBlock) void gap_partial_kernel(
   }
 }
 
+// Pass 1 with two x-adjacent voxels per lane (nx even, b and p aligned to
+// two elements): workgroup w walks tiles w, w + gridDim.x, ... of 128 x 8 x 24
+// voxels.  Per voxel the same fp32 z and g and the same fp64 terms as
+// gap_partial_kernel; a lane adds its first voxel's terms, then its second's.
+template <typename I, typename Off>
+__global__ __launch_bounds__(kPairBlock) void gap_partial_pair_kernel(
+    const float *__restrict__ b, const float *__restrict__ p0,
+    const float *__restrict__ p1, const float *__restrict__ p2, float lam,
+    ZxGeometry<I, Off> g, double *__restrict__ partial) {
+  constexpr int kW = kPairTileX + 2, kH = kPairTileY + 1;
+  __shared__ __attribute__((aligned(16))) float zring[3][kH][kW];
+  __shared__ double sh[3][kPairBlock];
+  const int lx = (int)(threadIdx.x % kPairLanes);
+  const int ly = (int)(threadIdx.x / kPairLanes);
+  // halo pair: wave 0 the upper y row, lanes 0..7 of wave 1 the pair just
+  // past the tile's last column
+  int hxl = -1, hyl = -1;
+  if (ly == 0) {
+    hxl = lx;
+    hyl = kPairTileY;
+  } else if (ly == 1 && lx < kPairTileY) {
+    hxl = kPairLanes;
+    hyl = lx;
+  }
+  const Off sy4 = g.sy4, sz4 = g.sz4;
+  const Off four = 4;
+  const f32x2 zero2 = {0.0f, 0.0f};
+  double s_norm = 0.0, s_gap = 0.0, s_fid = 0.0;
+
+  for (I t = (I)blockIdx.x; t < g.ntiles; t += (I)gridDim.x) {
+    I tx, ty, tz;
+    ordered_tile<I, Off>(xcd_tile(t, g.ntiles), g, tx, ty, tz);
+    const I x0 = tx * kPairTileX, y0 = ty * kPairTileY;
+    const I z0 = tz * g.planes;
+    const I z1 = (z0 + g.planes < g.nz) ? z0 + g.planes : g.nz;
+    // first voxel of the own pair and of the halo pair (nx is even, so the
+    // second voxel is inside whenever the first is)
+    const I x = x0 + 2 * lx, y = y0 + ly;
+    const I hx = x0 + 2 * hxl, hy = y0 + hyl;
+    const bool own_ok = x < g.nx && y < g.ny;
+    const bool halo_ok = hxl >= 0 && hx < g.nx && hy < g.ny;
+    const bool has_x2 = x + 2 < g.nx, has_y = y + 1 < g.ny;
+    const bool low_x = x > 0, low_y = y > 0;
+    const bool hlow_x = hx > 0, hlow_y = hy > 0;
+    const bool low_z = z0 > 0;
+    const Off oi = own_ok ? ((Off)x + (Off)g.nx * (Off)y) * four + (Off)z0 * sz4 : 0;
+    const Off oh = halo_ok ? ((Off)hx + (Off)g.nx * (Off)hy) * four + (Off)z0 * sz4 : 0;
+
+    // z at plane z0; the own p and b pairs of the column are carried
+    f32x2 pc0 = zero2, pc1 = zero2, pc2 = zero2, bc = zero2, ph2 = zero2, zc = zero2;
+    if (own_ok) {
+      pc0 = ld2(p0, oi);
+      pc1 = ld2(p1, oi);
+      pc2 = ld2(p2, oi);
+      bc = ldb2(b, oi);
+      const float a = lds(p0, low_x ? oi - four : oi);
+      const f32x2 e = ld2(p1, low_y ? oi - sy4 : oi);
+      const f32x2 f = ld2(p2, low_z ? oi - sz4 : oi);
+      zc = primal_pair(bc, pc0, low_x ? a : 0.0f, pc1, low_y ? e : zero2, pc2,
+                       low_z ? f : zero2, lam);
+      *(f32x2 *)&zring[0][ly][2 * lx] = zc;
+    }
+    if (halo_ok) {
+      ph2 = ld2(p2, oh);
+      const float a = lds(p0, hlow_x ? oh - four : oh);
+      const f32x2 e = ld2(p1, hlow_y ? oh - sy4 : oh);
+      const f32x2 f = ld2(p2, low_z ? oh - sz4 : oh);
+      *(f32x2 *)&zring[0][hyl][2 * hxl] =
+          primal_pair(ldb2(b, oh), ld2(p0, oh), hlow_x ? a : 0.0f, ld2(p1, oh),
+                      hlow_y ? e : zero2, ph2, low_z ? f : zero2, lam);
+    }
+
+    // Loads of the planes ahead, in two sets used on alternate planes: the
+    // plane step that consumes a set refills it with the plane three ahead,
+    // so every load has two plane steps to arrive.  The steps are unrolled
+    // (ring slot and set are constants) and every refill is unconditional:
+    // a plane past the last one the tile reads is replaced by that last
+    // plane, and lanes outside the volume read elements of its first column,
+    // which they never use.  So the wait for one set never has to cover the
+    // other set's loads.
+    struct Ahead {
+      f32x2 b, p0, p1, p2, p1l, hb, h0, h1, h2, h1l;
+      float p0l, h0l;
+    };
+    Ahead la[2];
+    const bool own_lx = own_ok && low_x, own_ly = own_ok && low_y;
+    const I last = z1 < g.nz - 1 ? z1 : g.nz - 1;  // last plane the tile reads
+    auto load_plane = [&](Ahead &l, I kp) {  // loads of plane min(kp, last)
+      const Off dz = (Off)((kp < last ? kp : last) - z0) * sz4;
+      if (halo_ok) {
+        const Off j = oh + dz;
+        l.hb = ldb2(b, j);
+        l.h0 = ld2(p0, j);
+        l.h1 = ld2(p1, j);
+        l.h2 = ld2(p2, j);
+        l.h0l = lds(p0, hlow_x ? j - four : j);
+        l.h1l = ld2(p1, hlow_y ? j - sy4 : j);
+      }
+      const Off j = oi + dz;
+      l.b = ldb2(b, j);
+      l.p0 = ld2(p0, j);
+      l.p1 = ld2(p1, j);
+      l.p2 = ld2(p2, j);
+      l.p0l = lds(p0, own_lx ? j - four : j);
+      l.p1l = ld2(p1, own_ly ? j - sy4 : j);
+    };
+    load_plane(la[0], z0 + 1);
+    load_plane(la[1], z0 + 2);
+
+#pragma unroll
+    for (int i = 0; i < kGapPairPlanes; ++i) {
+      Ahead &l = la[i % 2];  // plane k + 1
+      const int cur = i % 3, nxt = (i + 1) % 3;
+      const I k = z0 + i;
+      const bool in = k < z1;
+      const bool has_z = k + 1 < g.nz;
+      f32x2 zz = zero2;
+      if (in && has_z) {
+        if (own_ok) {
+          zz = primal_pair(l.b, l.p0, low_x ? l.p0l : 0.0f, l.p1, low_y ? l.p1l : zero2, l.p2,
+                           pc2, lam);
+          *(f32x2 *)&zring[nxt][ly][2 * lx] = zz;
+        }
+        if (halo_ok) {
+          *(f32x2 *)&zring[nxt][hyl][2 * hxl] =
+              primal_pair(l.hb, l.h0, hlow_x ? l.h0l : 0.0f, l.h1, hlow_y ? l.h1l : zero2,
+                          l.h2, ph2, lam);
+          ph2 = l.h2;
+        }
+      }
+      const f32x2 cb = l.b, c0 = l.p0, c1 = l.p1, c2 = l.p2;
+      if (i + 2 < kGapPairPlanes) load_plane(l, k + 3);
+      // ring of three planes: one barrier per plane (as in the step kernel)
+      __syncthreads();
+      if (in && own_ok) {
+        const float zx1 = zring[cur][ly][2 * lx + 2];
+        const f32x2 zy = *(const f32x2 *)&zring[cur][ly + 1][2 * lx];
+        double n, gp, f;
+        // first voxel: its upper x neighbour is the pair's second voxel
+        gap_terms(zc.x - zc.y, has_y ? zc.x - zy.x : 0.0f, has_z ? zc.x - zz.x : 0.0f,
+                  pc0.x, pc1.x, pc2.x, zc.x, bc.x, n, gp, f);
+        s_norm = s_norm + n;
+        s_gap = s_gap + gp;
+        s_fid = s_fid + f;
+        gap_terms(has_x2 ? zc.y - zx1 : 0.0f, has_y ? zc.y - zy.y : 0.0f,
+                  has_z ? zc.y - zz.y : 0.0f, pc0.y, pc1.y, pc2.y, zc.y, bc.y, n, gp, f);
+        s_norm = s_norm + n;
+        s_gap = s_gap + gp;
+        s_fid = s_fid + f;
+      }
+      zc = zz;
+      bc = cb;
+      pc0 = c0;
+      pc1 = c1;
+      pc2 = c2;
+    }
+    __syncthreads();  // the next tile rewrites ring slot 0
+  }
+  block_sum3<kPairBlock>(s_gap, s_norm, s_fid, sh);
+  if (threadIdx.x == 0) {
+    partial[3 * blockIdx.x + 0] = s_gap;
+    partial[3 * blockIdx.x + 1] = s_norm;
+    partial[3 * blockIdx.x + 2] = s_fid;
+  }
+}
+
 // Pass 2: one workgroup adds `count` partial triples in a fixed order.
 // out[0] = lambda * sum(|g| - g.p), out[1] = sum |g|, out[2] = 1/2 sum (z-b)^2.
 __global__ __launch_bounds__(kGapFinalBlock) void gap_final_kernel(
@@ -230,11 +409,30 @@ __global__ __launch_bounds__(kGapFinalBlock) void gap_final_kernel(
   }
 }
 
-// Number of partial triples (= workgroups of pass 1) for these dimensions.
+// Number of partial triples (= workgroups of pass 1) for these dimensions:
+// gap_grid for gap_partial_kernel, gap_pair_grid (never larger) for the pair
+// kernel.
 inline int gap_grid(int64_t nx, int64_t ny, int64_t nz) {
   const int64_t tiles = ((nx + kZxTileX - 1) / kZxTileX) * ((ny + kZxTileY - 1) / kZxTileY) *
                         ((nz + kZxPlanes - 1) / kZxPlanes);
   return (int)(tiles < kGapGrid ? tiles : kGapGrid);
+}
+
+inline int gap_pair_grid(int64_t nx, int64_t ny, int64_t nz) {
+  const int64_t tiles = ((nx + kPairTileX - 1) / kPairTileX) *
+                        ((ny + kPairTileY - 1) / kPairTileY) *
+                        ((nz + kGapPairPlanes - 1) / kGapPairPlanes);
+  return (int)(tiles < kGapPairGrid ? tiles : kGapPairGrid);
+}
+
+// Tiles of the pair kernel: pair_geometry with kGapPairPlanes planes per tile.
+template <typename I, typename Off>
+inline ZxGeometry<I, Off> gap_pair_geometry(int64_t nx, int64_t ny, int64_t nz) {
+  ZxGeometry<I, Off> g = pair_geometry<I, Off>(nx, ny, nz);
+  g.planes = (I)kGapPairPlanes;
+  g.tiles_z = (I)((nz + kGapPairPlanes - 1) / kGapPairPlanes);
+  g.ntiles = g.tiles_x * g.tiles_y * g.tiles_z;
+  return g;
 }
 
 }  // namespace tvfgp

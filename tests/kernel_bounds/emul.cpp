@@ -11,7 +11,7 @@
 // usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
 //   variant: fused | fused_nostream | fused_h | fused_nostream_h | pair | pair_nostream |
 //            pair_h | pair_nostream_h | reg_march | point | two_kernel | lds_march |
-//            primal | primal_h | gap | tb2 | tb2_h | cube | cube_32x8x2 | cube_64x8x1 |
+//            primal | primal_h | gap | gap_pair | tb2 | tb2_h | cube | cube_32x8x2 | cube_64x8x1 |
 //            cube_8x8x8 | cube_32x4x4
 //   (the pair variants need an even nx; with an odd one they report "ok" without running)
 //   wide: 1 instantiates the 64-bit offset / index path regardless of size
@@ -204,6 +204,17 @@ void run_ablation(const char *variant, const Bufs &v, int64_t nx, int64_t ny, in
     double *out = (double *)guarded(3 * sizeof(double), true, 98);
     run_grid((unsigned)count, kZxBlock, [&] {
       gap_partial_kernel<I, Off>(v.b, v.p[0], v.p[1], v.p[2], 0.01f, g, partial);
+    });
+    run_grid(1, kGapFinalBlock, [&] { gap_final_kernel(partial, count, 0.01, out); });
+  } else if (!strcmp(variant, "gap_pair")) {
+    if (nx % 2 != 0) return;  // the pair kernel takes even nx only
+    typedef typename std::conditional<sizeof(I) == 4, uint32_t, uint64_t>::type Off;
+    const ZxGeometry<I, Off> g = gap_pair_geometry<I, Off>(nx, ny, nz);
+    const int count = grid ? (int)grid : gap_pair_grid(nx, ny, nz);
+    double *partial = (double *)guarded((size_t)count * 3 * sizeof(double), true, 99);
+    double *out = (double *)guarded(3 * sizeof(double), true, 98);
+    run_grid((unsigned)count, kPairBlock, [&] {
+      gap_partial_pair_kernel<I, Off>(v.b, v.p[0], v.p[1], v.p[2], 0.01f, g, partial);
     });
     run_grid(1, kGapFinalBlock, [&] { gap_final_kernel(partial, count, 0.01, out); });
   } else if (!strcmp(variant, "lds_march")) {

@@ -13,6 +13,7 @@
 //           cube, cube_8x8x8  one step (m1) with the cube-tiled kernel
 //           lds_march  one step (m1) with the LDS z-march (8 planes per tile)
 //           gap    duality gap of p (three doubles written to <dir>/gap.bin)
+//           gap_pair  the same with two voxels per lane (even nx)
 //           tb2    two steps (m1 then m2) in one pass, p_in -> p_out
 //           tb2_h  the same with p and r stored as binary16 (files hold the
 //                  binary16 values as floats)
@@ -119,14 +120,27 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
                                                   g);
     });
     memcpy(p_out, p, 3 * n * sizeof(float));
-  } else if (!strcmp(kernel, "gap")) {
+  } else if (!strcmp(kernel, "gap") || !strcmp(kernel, "gap_pair")) {
     // duality gap of p: the three sums go to <dir>/gap.bin as doubles
-    const auto g = tvfgp::zx_geometry<I, Off>(nx, ny, nz);
-    const int count = grid ? (int)grid : tvfgp::gap_grid(nx, ny, nz);
+    const bool pair = !strcmp(kernel, "gap_pair");
+    if (pair && nx % 2 != 0) {
+      fprintf(stderr, "gap_pair needs an even nx\n");
+      exit(2);
+    }
+    const int count = grid ? (int)grid
+                           : pair ? tvfgp::gap_pair_grid(nx, ny, nz) : tvfgp::gap_grid(nx, ny, nz);
     std::vector<double> partial((size_t)count * 3);
-    run_grid((unsigned)count, tvfgp::kZxBlock, [&] {
-      tvfgp::gap_partial_kernel<I, Off>(b, p, p + n, p + 2 * n, lam, g, partial.data());
-    });
+    if (pair) {
+      const auto g = tvfgp::gap_pair_geometry<I, Off>(nx, ny, nz);
+      run_grid((unsigned)count, tvfgp::kPairBlock, [&] {
+        tvfgp::gap_partial_pair_kernel<I, Off>(b, p, p + n, p + 2 * n, lam, g, partial.data());
+      });
+    } else {
+      const auto g = tvfgp::zx_geometry<I, Off>(nx, ny, nz);
+      run_grid((unsigned)count, tvfgp::kZxBlock, [&] {
+        tvfgp::gap_partial_kernel<I, Off>(b, p, p + n, p + 2 * n, lam, g, partial.data());
+      });
+    }
     double out[3];
     run_grid(1, tvfgp::kGapFinalBlock,
              [&] { tvfgp::gap_final_kernel(partial.data(), count, (double)lam, out); });

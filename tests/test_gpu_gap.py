@@ -26,10 +26,14 @@ def tvf():
     return m
 
 
-def gpu_gap(tvf, b, p, lam):
+def gpu_gap(tvf, b, p, lam, b_offset=0):
+    """Gap triple of the device kernels; b_offset > 0 places b that many
+    elements into its allocation (misaligned for the pair pass when odd)."""
     nz, ny, nx = b.shape
     dev = torch.device("cuda")
-    bt = torch.from_numpy(np.ascontiguousarray(b)).to(dev)
+    store = torch.zeros(b.size + b_offset, dtype=torch.float32, device=dev)
+    bt = store[b_offset:].view(b.shape)
+    bt.copy_(torch.from_numpy(np.ascontiguousarray(b)))
     pt = torch.from_numpy(np.ascontiguousarray(p)).to(dev)
     out = torch.full((3,), float("nan"), dtype=torch.float64, device=dev)
     ws = torch.empty(tvf.gap_workspace_bytes(nx, ny, nz) // 8, dtype=torch.float64, device=dev)
@@ -64,6 +68,18 @@ def test_gap_ragged_random_dual(tvf, dims):
     exp = oracle.duality_gap(b, p0, 0.003)
     got = gpu_gap(tvf, b, p0, 0.003)
     assert_gap_close(got, exp, 0.003, str(dims))
+
+
+@pytest.mark.parametrize("dims", [(130, 17, 9), (258, 9, 19), (2, 11, 3), (512, 64, 24)],
+                         ids=lambda d: "x".join(map(str, d)))
+def test_gap_pair_and_one_voxel_passes(tvf, dims):
+    """Even nx with b and p aligned to two elements takes the two-voxels-per-
+    lane first pass; b one element into its allocation takes the one-voxel
+    pass.  Both agree with the oracle."""
+    b, p0, _ = phantoms.make_inputs(4, dims)
+    exp = oracle.duality_gap(b, p0, 0.003)
+    assert_gap_close(gpu_gap(tvf, b, p0, 0.003), exp, 0.003, "pair %s" % (dims,))
+    assert_gap_close(gpu_gap(tvf, b, p0, 0.003, b_offset=1), exp, 0.003, "one %s" % (dims,))
 
 
 def test_gap_deterministic(tvf):

@@ -25,10 +25,10 @@ SHAPES = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70)
           (126, 9, 4), (66, 10, 40), (130, 17, 33)]
 VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
             "pair_h", "pair_nostream_h", "reg_march", "point", "two_kernel", "lds_march", "primal",
-            "primal_h", "gap", "tb2", "tb2_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8",
+            "primal_h", "gap", "gap_pair", "tb2", "tb2_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8",
             "cube_32x4x4"]
 FOUR_PLANE = ("tb2", "tb2_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8", "cube_32x4x4", "fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
-              "pair_h", "pair_nostream_h", "point", "gap")
+              "pair_h", "pair_nostream_h", "point", "gap", "gap_pair")
 
 
 def compiler():

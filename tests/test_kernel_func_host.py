@@ -88,9 +88,12 @@ def test_lds_one_step(func, tmp_path, kernel, dims):
     assert_bits(rg, re, "r")
 
 
-@pytest.mark.parametrize("dims,grid", [((67, 19, 11), 0), ((130, 17, 9), 3), ((1, 1, 1), 0)],
-                         ids=lambda c: str(c))
-def test_duality_gap(func, tmp_path, dims, grid):
+@pytest.mark.parametrize("kernel,dims,grid", [
+    ("gap", (67, 19, 11), 0), ("gap", (130, 17, 9), 3), ("gap", (1, 1, 1), 0),
+    ("gap_pair", (130, 17, 9), 0), ("gap_pair", (258, 9, 19), 5), ("gap_pair", (2, 1, 1), 0),
+    ("gap_pair", (128, 8, 8), 0), ("gap_pair", (2, 11, 3), 0), ("gap_pair", (130, 9, 50), 0),
+    ("gap_pair", (2, 3, 30), 2)], ids=lambda c: str(c))
+def test_duality_gap(func, tmp_path, kernel, dims, grid):
     """The gap reduction's z exchange through LDS: sums within fp64 rounding of the oracle."""
     b, p0, r0 = inputs(dims)
     lam = 0.003
@@ -99,7 +102,7 @@ def test_duality_gap(func, tmp_path, dims, grid):
     b.tofile(os.path.join(d, "b.bin"))
     p0.tofile(os.path.join(d, "p.bin"))
     r0.tofile(os.path.join(d, "r.bin"))
-    r = subprocess.run([func, "gap", str(nx), str(ny), str(nz), repr(lam), "0", "0", d, "0",
+    r = subprocess.run([func, kernel, str(nx), str(ny), str(nz), repr(lam), "0", "0", d, "0",
                         str(grid)], capture_output=True, text=True, timeout=300)
     assert r.returncode == 0, r.stderr
     got = np.fromfile(os.path.join(d, "gap.bin"), np.float64)
