@@ -23,6 +23,9 @@ Besides the headline ms/step it reports:
                 launch by launch on the same data, with its own traffic record
   gap_kernel    time of one duality-gap evaluation of the final p (reads b and
                 p: 16 B per voxel) and the gap triple itself
+  repeats       the timed region run twice more (ms/step of all three, their
+                median and spread) and T0, the same solve with zero dual steps
+                per outer iteration, with (T - T0) / steps
   copy          bandwidth of a plain device copy of 2 x 1 GiB on the same box
   cpu_baseline  the CPU oracle (fp32, OpenMP) timed on the host cores on a
                 bounded sample: the first 10 outer iterations (100 steps) of
@@ -244,6 +247,21 @@ def main():
         wall_ms = (time.perf_counter() - t_wall) * 1e3
         region_ms = start.elapsed_time(stop)
 
+        # the same timed region twice more (spread across runs), and the solve
+        # with zero dual steps per outer iteration (T0: per step = (T - T0) / steps)
+        repeat_ms = []
+        for _ in range(2):
+            start.record(stream)
+            r_cur, r_nxt = run_steps(args.steps, r_cur, r_nxt)
+            stop.record(stream)
+            torch.cuda.synchronize()
+            repeat_ms.append(start.elapsed_time(stop))
+        start.record(stream)
+        run(r_cur, r_nxt, max(1, args.steps // n_inner), 0)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        t0_ms = start.elapsed_time(stop)
+
         # per-launch durations: an event pair around every launch (a launch of
         # the two-steps-per-pass kernel runs steps k and k+1, p_in -> p_out)
         n_launch = max(1, args.steps // spl)
@@ -267,6 +285,12 @@ def main():
         launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
 
     ms_per_step = region_ms / args.steps
+    runs = sorted([region_ms] + repeat_ms)
+    repeats = {"ms_per_step": [round(v / args.steps, 5) for v in [region_ms] + repeat_ms],
+               "median_ms_per_step": round(runs[1] / args.steps, 5),
+               "spread_pct": round(100.0 * (runs[-1] - runs[0]) / runs[1], 2),
+               "t0_ms": round(t0_ms, 4),
+               "t_minus_t0_ms_per_step": round((region_ms - t0_ms) / args.steps, 5)}
     step_bytes = (BYTES_PER_VOXEL_HALF if half else BYTES_PER_VOXEL[args.variant]) * nvox
     launch_avg_ms = float(np.mean(launch_ms))
     achieved = step_bytes / (launch_avg_ms * 1e-3) / 1e9
@@ -401,6 +425,7 @@ def main():
                      "launch_ms_min": round(float(np.min(launch_ms)), 5),
                      "launch_ms_max": round(float(np.max(launch_ms)), 5)},
         "one_step_kernel": one_step,
+        "repeats": repeats,
         "gap_kernel": gap,
         "copy": copy,
         "pct_of_copy": (round(100.0 * region_gbs / copy["gbps"], 1) if copy else None),

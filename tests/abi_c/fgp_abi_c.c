@@ -2,9 +2,10 @@
  * The C ABI used from plain C, without Python or torch (test infrastructure).
  *
  * Reads b (n floats), p and r (3n floats each) from <dir>, allocates device
- * buffers with the HIP runtime, runs tv_fgp_run (variant from argv) and
- * tv_primal through include/tv_fgp.h, and writes p, r (the buffer r_final
- * names) and z back to <dir>/{p,r,z}_out.bin.  The caller compares them with
+ * buffers with the HIP runtime, runs tv_fgp_run (variant from argv),
+ * tv_primal and tv_fgp_duality_gap through include/tv_fgp.h, and writes p, r
+ * (the buffer r_final names) and z back to <dir>/{p,r,z}_out.bin and the gap
+ * triple to <dir>/gap_out.bin (3 doubles).  The caller compares them with
  * the CPU oracle.  Every HIP and library status is checked; any failure
  * prints the call and exits non-zero.
  *
@@ -96,13 +97,35 @@ int main(int argc, char **argv) {
     fprintf(stderr, "tv_primal: %s\n", tv_fgp_status_string(st));
     return 4;
   }
+  const size_t gap_ws_bytes = tv_fgp_gap_workspace_bytes(nx, ny, nz);
+  void *gap_ws = NULL;
+  double *gap_dev = NULL, gap[3];
+  HIP_OK(hipMalloc(&gap_ws, gap_ws_bytes));
+  HIP_OK(hipMalloc((void **)&gap_dev, 3 * sizeof(double)));
+  st = tv_fgp_duality_gap(b, (const float *const *)P, lambda, nx, ny, nz, gap_dev, gap_ws,
+                          gap_ws_bytes, (void *)stream);
+  if (st != TV_OK) {
+    fprintf(stderr, "tv_fgp_duality_gap: %s\n", tv_fgp_status_string(st));
+    return 4;
+  }
   HIP_OK(hipStreamSynchronize(stream));
+  HIP_OK(hipMemcpy(gap, gap_dev, 3 * sizeof(double), hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(hp, p, 3 * bytes, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(hr, r_final ? rb : ra, 3 * bytes, hipMemcpyDeviceToHost));
   HIP_OK(hipMemcpy(hb, z, bytes, hipMemcpyDeviceToHost));
   write_floats(dir, "p_out.bin", hp, 3 * n);
   write_floats(dir, "r_out.bin", hr, 3 * n);
   write_floats(dir, "z_out.bin", hb, n);
+  {
+    char path[4096];
+    snprintf(path, sizeof path, "%s/gap_out.bin", dir);
+    FILE *f = fopen(path, "wb");
+    if (!f || fwrite(gap, sizeof(double), 3, f) != 3) {
+      fprintf(stderr, "cannot write %s\n", path);
+      exit(2);
+    }
+    fclose(f);
+  }
   HIP_OK(hipStreamDestroy(stream));
   HIP_OK(hipFree(b));
   HIP_OK(hipFree(p));
@@ -110,6 +133,8 @@ int main(int argc, char **argv) {
   HIP_OK(hipFree(rb));
   HIP_OK(hipFree(z));
   if (ws) HIP_OK(hipFree(ws));
+  HIP_OK(hipFree(gap_ws));
+  HIP_OK(hipFree(gap_dev));
   printf("ok %s r_final=%d\n", tv_fgp_variant_name(variant), r_final);
   return 0;
 }

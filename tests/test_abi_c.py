@@ -1,10 +1,10 @@
 """The C ABI from a plain C program (no Python binding, no torch).
 
 tests/abi_c/fgp_abi_c.c includes only include/tv_fgp.h and the HIP runtime
-header, allocates device memory with hipMalloc and calls tv_fgp_run and
-tv_primal.  The CPU test checks that it compiles and links against the built
-library; the GPU test runs it and compares its output with the CPU oracle bit
-for bit.
+header, allocates device memory with hipMalloc and calls tv_fgp_run,
+tv_primal and tv_fgp_duality_gap.  The CPU test checks that it compiles and
+links against the built library; the GPU test runs it and compares p, r and z
+with the CPU oracle bit for bit and the gap triple to fp64 summation error.
 """
 import os
 import shutil
@@ -59,3 +59,8 @@ def test_c_program_matches_oracle(tmp_path, variant):
     for name, exp in (("p", pe), ("r", re), ("z", ze)):
         got = np.fromfile(os.path.join(d, name + "_out.bin"), np.float32).reshape(exp.shape)
         assert np.array_equal(got.view(np.uint32), exp.view(np.uint32)), name
+    g, tv, fid = oracle.duality_gap(b, pe, 0.003)
+    got = np.fromfile(os.path.join(d, "gap_out.bin"), np.float64)
+    assert abs(got[0] - g) <= 1e-10 * 0.003 * tv, (got[0], g)
+    assert abs(got[1] - tv) <= 1e-10 * tv, (got[1], tv)
+    assert abs(got[2] - fid) <= 1e-10 * fid, (got[2], fid)
