@@ -68,9 +68,12 @@ def assert_bits(got, exp, label):
     assert bad == 0, "%s: %d values differ" % (label, bad)
 
 
-def test_fused_one_step(func, tmp_path):
-    """The emulator itself: the default kernel's single step equals the oracle's."""
-    b, p0, r0 = inputs((67, 19, 11))
+@pytest.mark.parametrize("dims", [(67, 19, 11), (65, 9, 6), (64, 8, 5), (1, 1, 1), (3, 17, 2)],
+                         ids=lambda d: str(d))
+def test_fused_one_step(func, tmp_path, dims):
+    """The default kernel's single step equals the oracle's (tiles of 4 planes,
+    ragged last tiles, a single voxel)."""
+    b, p0, r0 = inputs(dims)
     pg, rg = emulate(func, tmp_path, "fused", b, p0, r0, 0.003, np.float32(0.4), 0.0)
     pe, re = oracle.step(b, p0, r0, 0.003, np.float32(0.4))
     assert_bits(pg, pe, "p")
