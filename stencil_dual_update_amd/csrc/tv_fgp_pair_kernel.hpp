@@ -17,6 +17,12 @@
 // Pairs must be aligned: nx even (so every row and plane starts on an even
 // element) and every volume aligned to two of its elements.  The caller
 // checks this; other shapes take the one-voxel kernel.
+//
+// The eight plane steps of a tile are unrolled and every load is issued
+// unconditionally, so the prefetched plane stays in flight until the step
+// that uses it (a rolled loop rotates the prefetch registers with copies,
+// which wait for the loads).  Measured at 512^3: binary16 0.751 -> 0.709
+// ms/step, fp32 unchanged (1.29-1.34 vs 1.30).
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -154,21 +160,17 @@ __global__ __launch_bounds__(kPairBlock) void fused_pair_kernel(
                       hlow_y ? e : zero2, r2h, low_z ? f : zero2, lam);
     }
 
-    // registers holding the loads of the next plane (own pair and halo pair)
-    f32x2 nb = zero2, n0 = zero2, n1 = zero2, n2 = zero2, n1l = zero2;
+    // Loads of plane k+1, issued one plane ahead; the plane steps are
+    // unrolled and the loads unconditional (a plane past the last one the
+    // tile reads is replaced by that plane; threads outside the volume read
+    // its first column, never used).
+    const I last = z1 < g.nz - 1 ? z1 : g.nz - 1;
+    const bool own_lx = own_ok && low_x, own_ly = own_ok && low_y;
+    f32x2 nb, n0, n1, n2, n1l;
     f32x2 hb = zero2, h0 = zero2, h1 = zero2, h2 = zero2, h1l = zero2;
-    float n0l = 0.0f, h0l = 0.0f;
-    auto load_plane = [&](I kp) {  // loads of plane kp (kp < nz)
-      const Off dz = (Off)(kp - z0) * sz4;
-      if (own_ok) {
-        const Off j = oi + dz;
-        nb = ldb2(b, j);
-        n0 = ld2(ri0, j);
-        n1 = ld2(ri1, j);
-        n2 = ld2(ri2, j);
-        n0l = lds(ri0, low_x ? j - four : j);
-        n1l = ld2(ri1, low_y ? j - sy4 : j);
-      }
+    float n0l, h0l = 0.0f;
+    auto load_plane = [&](I kp) {
+      const Off dz = (Off)((kp < last ? kp : last) - z0) * sz4;
       if (halo_ok) {
         const Off j = oh + dz;
         hb = ldb2(b, j);
@@ -178,25 +180,30 @@ __global__ __launch_bounds__(kPairBlock) void fused_pair_kernel(
         h0l = lds(ri0, hlow_x ? j - four : j);
         h1l = ld2(ri1, hlow_y ? j - sy4 : j);
       }
+      const Off j = oi + dz;
+      nb = ldb2(b, j);
+      n0 = ld2(ri0, j);
+      n1 = ld2(ri1, j);
+      n2 = ld2(ri2, j);
+      n0l = lds(ri0, own_lx ? j - four : j);
+      n1l = ld2(ri1, own_ly ? j - sy4 : j);
     };
-    if (z0 + 1 < g.nz) load_plane(z0 + 1);
+    load_plane(z0 + 1);
 
-    int cur = 0;
-    for (I k = z0; k < z1; ++k) {
-      const int nxt = cur == 2 ? 0 : cur + 1;
+#pragma unroll
+    for (int i = 0; i < kPairPlanes; ++i) {
+      const I k = z0 + i;
+      if (k >= z1) break;
+      const int cur = i % 3, nxt = (i + 1) % 3;
       const bool has_z = k + 1 < g.nz;
-      const Off ok = oi + (Off)(k - z0) * sz4;
-      f32x2 pv0 = zero2, pv1 = zero2, pv2 = zero2;
-      if (own_ok) {
-        pv0 = kStreamP ? ld2_stream(p0, ok) : ld2(p0, ok);
-        pv1 = kStreamP ? ld2_stream(p1, ok) : ld2(p1, ok);
-        pv2 = kStreamP ? ld2_stream(p2, ok) : ld2(p2, ok);
-      }
-      // plane k+1 values in hand; start the loads of plane k+2
+      const Off ok = oi + (Off)i * sz4;
+      const f32x2 pv0 = kStreamP ? ld2_stream(p0, ok) : ld2(p0, ok);
+      const f32x2 pv1 = kStreamP ? ld2_stream(p1, ok) : ld2(p1, ok);
+      const f32x2 pv2 = kStreamP ? ld2_stream(p2, ok) : ld2(p2, ok);
       const f32x2 cb = nb, c0 = n0, c1 = n1, c2 = n2, c1l = n1l;
       const f32x2 db = hb, d0 = h0, d1 = h1, d2 = h2, d1l = h1l;
       const float c0l = n0l, d0l = h0l;
-      if (k + 1 < z1 && k + 2 < g.nz) load_plane(k + 2);
+      if (i + 1 < kPairPlanes) load_plane(k + 2);
 
       f32x2 zz = zero2;
       if (has_z) {
@@ -212,8 +219,6 @@ __global__ __launch_bounds__(kPairBlock) void fused_pair_kernel(
           r2h = d2;
         }
       }
-      // Ring of three planes: the slot written here was last read two planes
-      // ago, before the previous barrier, so one barrier per plane is enough.
       __syncthreads();
       if (own_ok) {
         const float zx1 = zring[cur][ly][2 * lx + 2];
@@ -236,7 +241,6 @@ __global__ __launch_bounds__(kPairBlock) void fused_pair_kernel(
       r0c = c0;
       r1c = c1;
       r2c = c2;
-      cur = nxt;
     }
     __syncthreads();  // the next tile rewrites ring slot 0
   }

@@ -14,6 +14,8 @@
 //           lds_march  one step (m1) with the LDS z-march (8 planes per tile)
 //           gap    duality gap of p (three doubles written to <dir>/gap.bin)
 //           gap_pair  the same with two voxels per lane (even nx)
+//           pair   one step of the two-voxels-per-lane kernel (even nx)
+//           pair_h the same with p and r stored as binary16
 //           tb2    two steps (m1 then m2) in one pass, p_in -> p_out
 //           tb2_h  the same with p and r stored as binary16 (files hold the
 //                  binary16 values as floats)
@@ -33,6 +35,7 @@
 #include "tv_fgp_cube_kernel.hpp"
 #include "tv_fgp_lds_kernel.hpp"
 #include "tv_fgp_gap_kernel.hpp"
+#include "tv_fgp_pair_kernel.hpp"
 
 thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
 
@@ -120,6 +123,40 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
                                                   g);
     });
     memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "pair")) {
+    if (nx % 2 != 0) {
+      fprintf(stderr, "pair needs an even nx\n");
+      exit(2);
+    }
+    const auto g = tvfgp::pair_geometry<I, Off>(nx, ny, nz);
+    run_grid(pick(g.ntiles, grid), tvfgp::kPairBlock, [&] {
+      tvfgp::fused_pair_kernel<I, Off, true, float>(b, p, p + n, p + 2 * n, r, r + n,
+                                                    r + 2 * n, r_out, r_out + n,
+                                                    r_out + 2 * n, lam, c, m1, g);
+    });
+    memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "pair_h")) {
+    // binary16 dual: the inputs must be binary16 values (converted exactly)
+    if (nx % 2 != 0) {
+      fprintf(stderr, "pair_h needs an even nx\n");
+      exit(2);
+    }
+    typedef _Float16 h;
+    std::vector<h> ph(3 * n), rh(3 * n), roh(3 * n);
+    for (size_t i = 0; i < 3 * n; ++i) {
+      ph[i] = (h)p[i];
+      rh[i] = (h)r[i];
+    }
+    const auto g = tvfgp::pair_geometry<I, Off>(nx, ny, nz);
+    h *P = ph.data(), *R = rh.data(), *RO = roh.data();
+    run_grid(pick(g.ntiles, grid), tvfgp::kPairBlock, [&] {
+      tvfgp::fused_pair_kernel<I, Off, true, h>(b, P, P + n, P + 2 * n, R, R + n, R + 2 * n,
+                                                RO, RO + n, RO + 2 * n, lam, c, m1, g);
+    });
+    for (size_t i = 0; i < 3 * n; ++i) {
+      p_out[i] = (float)ph[i];
+      r_out[i] = (float)roh[i];
+    }
   } else if (!strcmp(kernel, "gap") || !strcmp(kernel, "gap_pair")) {
     // duality gap of p: the three sums go to <dir>/gap.bin as doubles
     const bool pair = !strcmp(kernel, "gap_pair");

@@ -80,6 +80,30 @@ def test_fused_one_step(func, tmp_path, dims):
     assert_bits(rg, re, "r")
 
 
+@pytest.mark.parametrize("dims", [(130, 17, 11), (2, 1, 1), (128, 8, 8), (258, 9, 19), (4, 3, 2)],
+                         ids=lambda d: str(d))
+def test_pair_one_step(func, tmp_path, dims):
+    """The two-voxels-per-lane kernel's single step equals the oracle's (8-plane
+    tiles, ragged x, y and z tails)."""
+    b, p0, r0 = inputs(dims)
+    pg, rg = emulate(func, tmp_path, "pair", b, p0, r0, 0.003, np.float32(0.4), 0.0)
+    pe, re = oracle.step(b, p0, r0, 0.003, np.float32(0.4))
+    assert_bits(pg, pe, "p")
+    assert_bits(rg, re, "r")
+
+
+@pytest.mark.parametrize("dims", [(130, 17, 11), (2, 3, 9)], ids=lambda d: str(d))
+def test_pair_one_step_binary16(func, tmp_path, dims):
+    """The binary16 one-step kernel equals one step of the oracle's half mode."""
+    b, p0, r0 = inputs(dims)
+    ph, rh = oracle.f32_to_f16_bits(p0), oracle.f32_to_f16_bits(r0)
+    pg, rg = emulate(func, tmp_path, "pair_h", b, oracle.f16_bits_to_f32(ph),
+                     oracle.f16_bits_to_f32(rh), 0.003, np.float32(oracle.momentum(1)), 0.0)
+    pe, re = oracle.run_half(b, ph, rh, 0.003, 1, 1)
+    assert np.array_equal(oracle.f32_to_f16_bits(pg), pe)
+    assert np.array_equal(oracle.f32_to_f16_bits(rg), re)
+
+
 @pytest.mark.parametrize("kernel", ["cube", "cube_8x8x8", "lds_march"])
 @pytest.mark.parametrize("dims", [(37, 19, 11), (16, 8, 4), (1, 1, 1), (70, 9, 19)],
                          ids=lambda d: str(d))
