@@ -61,7 +61,8 @@ extern "C" {
                                 z, z is computed once per point and exchanged
                                 through LDS, r is read through the caches            */
 #define TV_FGP_LDS_MARCH  1  /* ablation: 64x4 x-y tiles march along z with two
-                                planes of z in LDS and two barriers per plane        */
+                                planes of r and of z staged in LDS and three
+                                barriers per plane                                   */
 #define TV_FGP_TWO_KERNEL 2  /* ablation: a primal kernel writes z to the workspace,
                                 a dual kernel reads it (18 volumes per step)         */
 #define TV_FGP_POINT      3  /* ablation: one voxel per thread, z recomputed at the
@@ -302,8 +303,10 @@ float tv_fgp_momentum(int k);
 /* Static, NUL-terminated description of a status code. */
 const char *tv_fgp_status_string(int status);
 
-/* Name of a variant ("fused", "lds_march", "two_kernel", "point",
-   "reg_march"), or NULL. */
+/* Static name of a variant: "fused", "lds_march", "two_kernel", "point",
+   "reg_march", "pair", "tb2", "cube", "cube_32x8x2", "cube_64x8x1",
+   "cube_8x8x8", "cube_32x4x4" for TV_FGP_FUSED .. TV_FGP_CUBE_32x4x4; NULL
+   for any other value.  Host-only. */
 const char *tv_fgp_variant_name(int variant);
 
 #ifdef __cplusplus
