@@ -6,7 +6,8 @@ kernels from int32 to int64 indices, and the grid is smaller than the tile
 count, so workgroups loop over tiles.  Each variant runs two steps; sampled
 voxels (corners, faces, interior, tile and group edges) are compared with the
 CPU oracle on sub-boxes of the inputs (after K steps a voxel depends only on
-inputs within K voxels of it).
+inputs within K voxels of it).  The duality-gap reduction is checked on the
+same volume against the oracle's gap of the whole volume.
 """
 import numpy as np
 import pytest
@@ -69,3 +70,49 @@ def test_volume_past_2_31_voxels_all_variants():
             assert np.float32(gz) == ze, (variant, c, gz, ze)
     del bt, p, ra, rb, ws, ws3
     torch.cuda.empty_cache()
+
+
+def test_duality_gap_past_2_31_voxels():
+    """Both first passes of the gap reduction (voxel pairs; one voxel, taken
+    when b is misaligned) on their 64-bit offset paths, against the oracle's
+    gap of the same p over the whole volume.  The oracle adds 2.2e9 terms
+    one after another in fp64, so the comparison allows 1e-8 relative (its
+    own rounding error is below n * 2^-53 ~ 2.4e-7 in the worst case and
+    ~sqrt(n) * 2^-53 ~ 5e-12 typically)."""
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import stencil_dual_update_amd as tvf
+    nx, ny, nz = DIMS
+    n = nx * ny * nz
+    free, _ = torch.cuda.mem_get_info()
+    need = 12 * n * 4
+    assert free > need, "needs %.0f GB of device memory, %.0f GB free" % (need / 1e9, free / 1e9)
+    b = phantoms.make_uniform(DIMS, seed=12, lo=-0.01, hi=0.05)
+    dev = torch.device("cuda")
+    store = torch.empty(n + 1, dtype=torch.float32, device=dev)
+    b_al = torch.from_numpy(b).to(dev)          # aligned: the pair pass
+    b_mis = store[1:].view(nz, ny, nx)          # one element in: the one-voxel pass
+    b_mis.copy_(b_al)
+    p = torch.zeros((3, nz, ny, nx), device=dev)
+    ra = torch.zeros_like(p)
+    rb = torch.empty_like(p)
+    tvf.tv_fgp_run(b_al, p, ra, rb, LAM, 1, 3)  # a dual field with |p| <= 1, not all zero
+    del ra, rb
+    ws = torch.empty(tvf.gap_workspace_bytes(nx, ny, nz) // 8, dtype=torch.float64, device=dev)
+    got = []
+    for bt in (b_al, b_mis):
+        out = torch.full((3,), float("nan"), dtype=torch.float64, device=dev)
+        tvf.tv_fgp_duality_gap(bt, p, LAM, out, ws)
+        torch.cuda.synchronize()
+        got.append(out.cpu().numpy())
+    ph = p.cpu().numpy()
+    del store, b_al, b_mis, p, ws
+    torch.cuda.empty_cache()
+    g, tv, fid = oracle.duality_gap(b, ph, LAM)
+    assert tv > 0 and fid > 0
+    for label, v in zip(("pair", "one voxel"), got):
+        assert abs(v[0] - g) <= 1e-8 * LAM * tv, (label, v[0], g)
+        assert abs(v[1] - tv) <= 1e-8 * tv, (label, v[1], tv)
+        assert abs(v[2] - fid) <= 1e-8 * fid, (label, v[2], fid)
+    # the two passes sum in different orders; both are far more accurate
+    # than the tolerance above
+    assert abs(got[0][1] - got[1][1]) <= 1e-11 * tv
