@@ -7,7 +7,9 @@ count, so workgroups loop over tiles.  Each variant runs two steps; sampled
 voxels (corners, faces, interior, tile and group edges) are compared with the
 CPU oracle on sub-boxes of the inputs (after K steps a voxel depends only on
 inputs within K voxels of it).  The duality-gap reduction is checked on the
-same volume against the oracle's gap of the whole volume.
+same volume against the oracle's gap of the whole volume, and the binary16
+runs (one and two steps per pass) on sampled voxels against the oracle's half
+mode.
 """
 import numpy as np
 import pytest
@@ -116,3 +118,48 @@ def test_duality_gap_past_2_31_voxels():
     # the two passes sum in different orders; both are far more accurate
     # than the tolerance above
     assert abs(got[0][1] - got[1][1]) <= 1e-11 * tv
+
+
+@pytest.mark.parametrize("two_per_pass", [False, True], ids=["one_step", "two_steps"])
+def test_binary16_past_2_31_voxels(two_per_pass):
+    """The binary16 paths (the pair kernel and the two-steps-per-pass kernel)
+    on their 64-bit offset paths: three steps from p = r = 0 (an odd count, so
+    the two-step run also takes one single step), sampled voxels against the
+    oracle's half mode on sub-boxes, bit for bit on the stored binary16."""
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import stencil_dual_update_amd as tvf
+    nx, ny, nz = DIMS
+    n = nx * ny * nz
+    free, _ = torch.cuda.mem_get_info()
+    need = n * 4 + 12 * n * 2
+    assert free > need, "needs %.0f GB of device memory, %.0f GB free" % (need / 1e9, free / 1e9)
+    b = phantoms.make_uniform(DIMS, seed=13, lo=-0.01, hi=0.05)
+    dev = torch.device("cuda")
+    bt = torch.from_numpy(b).to(dev)
+    p = torch.zeros((3, nz, ny, nx), dtype=torch.float16, device=dev)
+    ra = torch.zeros_like(p)
+    rb = torch.empty_like(p)
+    n_outer, n_inner = 1, 3
+    if two_per_pass:
+        ws = torch.empty_like(p)
+        where = tvf.tv_fgp_run2_h(bt, p, ws, ra, rb, LAM, n_outer, n_inner)
+    else:
+        where = tvf.tv_fgp_run_h(bt, p, ra, rb, LAM, n_outer, n_inner)
+    torch.cuda.synchronize()
+    r = rb if where else ra
+    K = n_outer * n_inner
+    pts = [(0, 0, 0), (nz - 1, ny - 1, nx - 1), (nz // 2, ny // 2, nx // 2), (7, 1299, 0),
+           (1199, 0, 1399), (600, 8 * 81, 64 * 16), (601, 8 * 81 - 1, 128 * 8 - 1),
+           (1100, 517, 1023), (3, 4, 1024), (1196, 1297, 700)]
+    for c in pts:
+        sl = tuple(slice(max(0, ci - K - 1), min(s, ci + K + 2)) for ci, s in zip(c, b.shape))
+        loc = tuple(ci - s.start for ci, s in zip(c, sl))
+        sub = np.ascontiguousarray(b[sl])
+        z0 = np.zeros((3,) + sub.shape, np.uint16)
+        pe, re = oracle.run_half(sub, z0, z0, LAM, n_outer, n_inner)
+        gp = p[:, c[0], c[1], c[2]].cpu().numpy().view(np.uint16)
+        gr = r[:, c[0], c[1], c[2]].cpu().numpy().view(np.uint16)
+        assert np.array_equal(gp, pe[(slice(None),) + loc]), ("p", c, gp, pe[(slice(None),) + loc])
+        assert np.array_equal(gr, re[(slice(None),) + loc]), ("r", c, gr, re[(slice(None),) + loc])
+    del bt, p, ra, rb
+    torch.cuda.empty_cache()
