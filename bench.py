@@ -2,16 +2,17 @@
 
 Prints one JSON line.  The metric is ms per FGP step over the whole volume;
 the default workload is the 512^3 ellipsoid phantom, 20 outer x 10 inner
-steps, lambda = 0.002, run by tv_fgp_run with the two-steps-per-pass kernel
-(variant tb2: steps k and k+1 of an outer iteration in one launch, bit for
-bit the same as two one-step launches).  The timed region runs exactly
---steps steps (in outer iterations of 10, momentum restarted at each) on one
-stream, bracketed by device synchronisation; inputs are resident in HBM
-before it starts.
+steps, lambda = 0.002, run by tv_fgp_run with the three-steps-per-pass kernel
+(variant tb3: three consecutive steps in one launch, bit for bit the same as
+three one-step launches; 200 steps = 66 launches of three and one of two).
+The timed region runs exactly --steps steps (in outer iterations of 10,
+momentum restarted at each) on one stream, bracketed by device
+synchronisation; inputs are resident in HBM before it starts.
 
 Besides the headline ms/step it reports:
   roofline      algorithmic bytes per launch (52 B per voxel: read b, r (3),
-                p (3); write p (3), r (3); for tb2 that covers two steps) over
+                p (3); write p (3), r (3); for tb3 that covers three steps)
+                over
                 the average launch duration, timed with events around every
                 launch on the launch stream, against MI355X's 8 TB/s HBM peak;
                 `traffic` is the HBM bytes per launch from the rocprofv3
@@ -23,6 +24,8 @@ Besides the headline ms/step it reports:
                 launch by launch on the same data, with its own traffic record
   gap_kernel    time of one duality-gap evaluation of the final p (reads b and
                 p: 16 B per voxel) and the gap triple itself
+  vs_one_step_roofline  the time a one-step pass needs at the 8 TB/s peak
+                (52 B per voxel per step) and its ratio to the measured ms/step
   repeats       the timed region run twice more (ms/step of all three, their
                 median and spread) and T0, the same solve with zero dual steps
                 per outer iteration, with (T - T0) / steps
@@ -48,9 +51,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 HBM_PEAK_GBS = 8000.0
 # algorithmic bytes per voxel per launch, and FGP steps per launch
 BYTES_PER_VOXEL = {"fused": 52, "lds_march": 52, "point": 52, "reg_march": 52, "pair": 52,
-                   "two_kernel": 72, "tb2": 52, "cube": 52, "cube_32x8x2": 52,
+                   "two_kernel": 72, "tb2": 52, "tb3": 52, "cube": 52, "cube_32x8x2": 52,
                    "cube_64x8x1": 52, "cube_8x8x8": 52, "cube_32x4x4": 52}
-STEPS_PER_LAUNCH = {"tb2": 2}
+STEPS_PER_LAUNCH = {"tb2": 2, "tb3": 3}
 BYTES_PER_VOXEL_HALF = 28
 METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
 
@@ -58,6 +61,8 @@ METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
 # from: a committed traffic record (profiles/traffic_<variant>_512.json) is
 # reported only while these sources are unchanged.
 KERNELS = {
+    "tb3": ("tb3_kernel", ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp",
+                           "tv_fgp_tb2_kernel.hpp", "tv_fgp_tb3_kernel.hpp", "tv_fgp_tb3.hip")),
     "tb2": ("tb2_kernel", ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp",
                            "tv_fgp_tb2_kernel.hpp", "tv_fgp_tb2.hip")),
     "fused": ("fused_zx_kernel", ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp",
@@ -164,7 +169,9 @@ def parse():
 def main():
     args = parse()
     if args.variant is None:
-        args.variant = "tb2"
+        # fp32: three steps per pass; binary16: two (its pass is bound by
+        # arithmetic, which a third level of halo would add to)
+        args.variant = "tb2" if args.storage == "half" else "tb3"
     if args.traffic:
         write_traffic(*args.traffic, args.variant)
         return 0
@@ -204,7 +211,7 @@ def main():
     ra = p.clone()
     rb = torch.empty_like(ra)
     ws = (torch.empty_like(b) if variant == tvf.TWO_KERNEL else
-          torch.empty_like(p) if variant == tvf.TB2 else None)
+          torch.empty_like(p) if variant in (tvf.TB2, tvf.TB3) else None)
     spl = STEPS_PER_LAUNCH.get(args.variant, 1)
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
@@ -263,7 +270,8 @@ def main():
         t0_ms = start.elapsed_time(stop)
 
         # per-launch durations: an event pair around every launch (a launch of
-        # the two-steps-per-pass kernel runs steps k and k+1, p_in -> p_out)
+        # the two- or three-steps-per-pass kernel runs steps k, k+1 (, k+2),
+        # p_in -> p_out)
         n_launch = max(1, args.steps // spl)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_launch)]
@@ -271,7 +279,12 @@ def main():
         for q in range(n_launch):
             k = q * spl
             evs[q][0].record(stream)
-            if spl == 2:
+            if spl == 3:
+                tvf.tv_fgp_step3(b, p_cur, p_alt, r_cur, r_nxt, lam,
+                                 *(tvf.momentum((k + i) % n_inner + 1) for i in range(3)),
+                                 stream=stream)
+                p_cur, p_alt = p_alt, p_cur
+            elif spl == 2:
                 step2 = tvf.tv_fgp_step2_h if half else tvf.tv_fgp_step2
                 step2(b, p_cur, p_alt, r_cur, r_nxt, lam, tvf.momentum(k % n_inner + 1),
                       tvf.momentum((k + 1) % n_inner + 1), stream=stream)
@@ -426,6 +439,13 @@ def main():
                      "launch_ms_max": round(float(np.max(launch_ms)), 5)},
         "one_step_kernel": one_step,
         "repeats": repeats,
+        # a pass that does one step moves 52 B per voxel per step: its time at
+        # the 8 TB/s peak is the one-step roofline, which several steps per
+        # pass can beat
+        "vs_one_step_roofline": ({
+            "one_step_ms_at_peak": round(52 * nvox / (HBM_PEAK_GBS * 1e9) * 1e3, 5),
+            "ratio": round(52 * nvox / (HBM_PEAK_GBS * 1e9) * 1e3 / ms_per_step, 3)}
+            if not half else None),
         "gap_kernel": gap,
         "copy": copy,
         "pct_of_copy": (round(100.0 * region_gbs / copy["gbps"], 1) if copy else None),

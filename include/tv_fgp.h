@@ -89,6 +89,13 @@ extern "C" {
 #define TV_FGP_CUBE_64x8x1 9 /* ... 64x8x1 (one plane per cube)                   */
 #define TV_FGP_CUBE_8x8x8 10 /* ... 8x8x8                                         */
 #define TV_FGP_CUBE_32x4x4 11 /* ... 32x4x4                                       */
+#define TV_FGP_TB3        12 /* three steps per pass over HBM: step one runs on the
+                                tile grown by two voxels, step two on the tile
+                                grown by one, both stay on chip, step three is
+                                written (52 B per voxel per three steps).  Used
+                                by tv_fgp_run and tv_fgp_solve with a workspace
+                                of three volumes, like TV_FGP_TB2; a single step
+                                (tv_fgp_step_ex) runs the fused kernel            */
 
 /*
  * One FGP step ("TV solver: the FGP step on the GPU", section "What one step
@@ -140,12 +147,15 @@ int tv_fgp_step_ex(const float *b, float *const p[3],
  * With n_outer * n_inner == 0 nothing is enqueued and *r_final = 0.
  * Other arguments as tv_fgp_step_ex.  p, r_a, r_b and z_ws must not overlap
  * each other or b.
- * TV_FGP_TB2: z_ws holds three volumes (tv_fgp_workspace_bytes), used as a
- * second p buffer: the steps of each outer iteration run in pairs, one
- * launch per pair, p alternating between the caller's p and z_ws; an odd
- * last step runs the fused kernel in place; if p ends in z_ws it is copied
- * back into p on the stream.  Results equal those of the other variants bit
- * for bit; only the buffer named by r_final may differ.
+ * TV_FGP_TB2, TV_FGP_TB3: z_ws holds three volumes (tv_fgp_workspace_bytes),
+ * used as a second p buffer.  The n_outer * n_inner steps run as one sequence
+ * in passes of two (TB2) or of three ending in twos (TB3: 10 = 3+3+2+2,
+ * 200 = 66 x 3 + 2), one launch per pass, p alternating between the caller's
+ * p and z_ws; a pass may span two outer iterations, each step taking the
+ * momentum of its own position; a single step left over runs the fused kernel
+ * in place; if p ends in z_ws it is copied back into p on the stream.
+ * Results equal those of the other variants bit for bit; only the buffer
+ * named by r_final may differ.
  */
 int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
                float *const r_b[3], float lambda, int n_outer, int n_inner,
@@ -169,6 +179,20 @@ int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
 int tv_fgp_step2(const float *b, const float *const p_in[3], float *const p_out[3],
                  const float *const r_in[3], float *const r_out[3], float lambda,
                  float m1, float m2, int64_t nx, int64_t ny, int64_t nz, void *stream);
+
+/*
+ * Three consecutive FGP steps ("TV solver: the FGP step on the GPU", section
+ * "What one step does", applied three times) in one pass over the volumes,
+ * with momenta m1, m2, m3.  Reads b, p_in and r_in once, writes p_out and
+ * r_out once (52 bytes per voxel for three steps).  The result is bit for bit
+ * that of tv_fgp_step(m1), tv_fgp_step(m2), tv_fgp_step(m3), with p ending in
+ * p_out and the third step's momentum copy in r_out.  Arguments, overlap
+ * rules and status codes as tv_fgp_step2; m3 must be finite.
+ */
+int tv_fgp_step3(const float *b, const float *const p_in[3], float *const p_out[3],
+                 const float *const r_in[3], float *const r_out[3], float lambda,
+                 float m1, float m2, float m3, int64_t nx, int64_t ny, int64_t nz,
+                 void *stream);
 
 /*
  * Primal read-out z = max(b - lambda * L(p), 0) from a dual field p, with the
@@ -288,8 +312,8 @@ int tv_fgp_solve(const float *b, float *const p[3], float *const r_a[3],
 
 /*
  * Bytes of workspace a run of `variant` needs at these dimensions:
- * nx*ny*nz*4 for TV_FGP_TWO_KERNEL (z), 3*nx*ny*nz*4 for TV_FGP_TB2 (a
- * second p, three consecutive volumes), 0 for the others.  Returns 0 for
+ * nx*ny*nz*4 for TV_FGP_TWO_KERNEL (z), 3*nx*ny*nz*4 for TV_FGP_TB2 and
+ * TV_FGP_TB3 (a second p, three consecutive volumes), 0 for the others.  Returns 0 for
  * invalid dimensions or an unknown variant.
  */
 size_t tv_fgp_workspace_bytes(int variant, int64_t nx, int64_t ny, int64_t nz);
@@ -305,7 +329,7 @@ const char *tv_fgp_status_string(int status);
 
 /* Static name of a variant: "fused", "lds_march", "two_kernel", "point",
    "reg_march", "pair", "tb2", "cube", "cube_32x8x2", "cube_64x8x1",
-   "cube_8x8x8", "cube_32x4x4" for TV_FGP_FUSED .. TV_FGP_CUBE_32x4x4; NULL
+   "cube_8x8x8", "cube_32x4x4", "tb3" for TV_FGP_FUSED .. TV_FGP_TB3; NULL
    for any other value.  Host-only. */
 const char *tv_fgp_variant_name(int variant);
 

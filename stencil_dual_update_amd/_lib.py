@@ -29,13 +29,15 @@ REG_MARCH = 4
 PAIR = 5
 TB2 = 6
 CUBE = 7
+TB3 = 12
 VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
             "point": POINT, "reg_march": REG_MARCH, "pair": PAIR,
             "tb2": TB2, "cube": CUBE, "cube_32x8x2": 8, "cube_64x8x1": 9, "cube_8x8x8": 10,
-            "cube_32x4x4": 11}
+            "cube_32x4x4": 11, "tb3": TB3}
 
 # Names declared in include/tv_fgp.h, in declaration order.
-EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_fgp_step2", "tv_primal",
+EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_fgp_step2", "tv_fgp_step3",
+           "tv_primal",
            "tv_fgp_step_h", "tv_fgp_run_h", "tv_fgp_step2_h", "tv_fgp_run2_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
            "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_status_string",
            "tv_fgp_variant_name")
@@ -76,6 +78,8 @@ def _load():
                                ctypes.POINTER(ctypes.c_int)]
     lib.tv_fgp_step2.restype = ctypes.c_int
     lib.tv_fgp_step2.argtypes = [P, P3, P3, P3, P3, F, F, F, I64, I64, I64, P]
+    lib.tv_fgp_step3.restype = ctypes.c_int
+    lib.tv_fgp_step3.argtypes = [P, P3, P3, P3, P3, F, F, F, F, I64, I64, I64, P]
     lib.tv_primal.restype = ctypes.c_int
     lib.tv_primal.argtypes = [P, P3, P, F, I64, I64, I64, P]
     lib.tv_fgp_step_h.restype = ctypes.c_int
@@ -175,8 +179,8 @@ def _check_volume(t, shape, what):
 
 
 def _check_ws(t, shape, variant, what="z_ws"):
-    """The run workspace: one volume, or three (a (3, nz, ny, nx) tensor) for TB2."""
-    if variant == TB2 and t is not None and not isinstance(t, int):
+    """The run workspace: one volume, or three (a (3, nz, ny, nx) tensor) for TB2 and TB3."""
+    if variant in (TB2, TB3) and t is not None and not isinstance(t, int):
         _check_volume(t, (3,) + shape, what)
     else:
         _check_volume(t, shape, what)
@@ -285,6 +289,18 @@ def tv_fgp_step2(b, p_in, p_out, r_in, r_out, lam, m1, m2, stream=None, dims=Non
                           _field(r_in, shape, "r_in"), _field(r_out, shape, "r_out"),
                           float(lam), float(m1), float(m2), nx, ny, nz, _stream(stream))
     _raise(st, "tv_fgp_step2")
+
+
+def tv_fgp_step3(b, p_in, p_out, r_in, r_out, lam, m1, m2, m3, stream=None, dims=None):
+    """Three FGP steps (momentum m1, m2, m3) in one pass: p_in -> p_out, r_in -> r_out."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    st = lib.tv_fgp_step3(_addr(b), _field(p_in, shape, "p_in"), _field(p_out, shape, "p_out"),
+                          _field(r_in, shape, "r_in"), _field(r_out, shape, "r_out"),
+                          float(lam), float(m1), float(m2), float(m3), nx, ny, nz,
+                          _stream(stream))
+    _raise(st, "tv_fgp_step3")
 
 
 def tv_primal(b, p, z, lam, stream=None, dims=None):

@@ -93,45 +93,60 @@ tvfgp::StepArgs make_step(const float *b, float *const p[3],
 
 int launch_status(int rc) { return rc == 0 ? TV_OK : TV_ERR_LAUNCH; }
 
-// Inner loop of the two-steps-per-pass kernels, for fp32 (T = float) and
-// binary16 (T = uint16_t) duals: the steps of each outer iteration run in
-// pairs, one pass(p_in, p_out, r_in, r_out, m_k, m_k+1) each, p alternating
-// between the caller's p and the workspace p_ws; an odd last step of an outer
-// iteration runs single(p, r_in, r_out, m) in place; if p ends in the
-// workspace it is copied back.  `where` (0: r_a holds r, 1: r_b) flips after
-// every launch.  pass and single return 0 on success.
-template <typename T, typename Pass, typename Single>
-int enqueue_pairs(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], int n_outer,
-                  int n_inner, size_t vol_bytes, void *stream, int *where, Pass pass,
-                  Single single) {
+// Inner loop of the multi-step-per-pass kernels, for fp32 (T = float) and
+// binary16 (T = uint16_t) duals.  The n_outer x n_inner steps run as one
+// sequence cut into passes of up to max_group (2 or 3) steps: pass3(p_in,
+// p_out, r_in, r_out, m1, m2, m3), pass2(..., m1, m2), each with p
+// alternating between the caller's p and the workspace p_ws, and a single
+// step single(p, r_in, r_out, m) in place when one step is left.  The
+// momentum of a step is m_k for its position k in its outer iteration (the
+// sequence restarts at each outer iteration, and p and r carry over), so a
+// pass may span two outer iterations and the result is the same as step by
+// step.  Threes end in twos rather than a single step where they can
+// (200 = 66 x 3 + 2, 10 = 3 + 3 + 2 + 2).  If p ends in the workspace it is
+// copied back.  `where` (0: r_a holds r, 1: r_b) flips after every launch.
+// The callables return 0 on success.
+template <typename T, typename Pass3, typename Pass2, typename Single>
+int enqueue_grouped(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], int n_outer,
+                    int n_inner, size_t vol_bytes, void *stream, int *where, int max_group,
+                    Pass3 pass3, Pass2 pass2, Single single) {
   const size_t n = vol_bytes / sizeof(T);
   T *const ws[3] = {p_ws, p_ws + n, p_ws + 2 * n};
   T *const *cur = p;
   T *const *alt = ws;
-  for (int o = 0; o < n_outer; ++o) {
-    double t = 1.0;
-    for (int k = 1; k <= n_inner;) {
-      const int todo = n_inner - k + 1 >= 2 ? 2 : 1;
-      float m[2] = {0.0f, 0.0f};
-      // m_k and m_{k+1}, evaluated as in the one-step loop
-      for (int s = 0; s < todo; ++s) {
-        const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
-        m[s] = (float)((t - 1.0) / t_next);
-        t = t_next;
-      }
-      T *const *in = *where ? r_b : r_a;
-      T *const *out = *where ? r_a : r_b;
-      if (todo == 2) {
-        if (pass(cur, alt, in, out, m[0], m[1]) != 0) return TV_ERR_LAUNCH;
-        T *const *tmp = cur;
-        cur = alt;
-        alt = tmp;
-      } else if (single(cur, in, out, m[0]) != 0) {
-        return TV_ERR_LAUNCH;
-      }
-      *where ^= 1;
-      k += todo;
+  const int64_t total = (int64_t)n_outer * n_inner;
+  double t = 1.0;
+  int k_in = 0;  // steps already taken in the current outer iteration
+  for (int64_t s = 0; s < total;) {
+    const int64_t left = total - s;
+    int todo;
+    if (max_group >= 3 && (left >= 5 || left == 3))
+      todo = 3;
+    else
+      todo = left >= 2 ? 2 : 1;
+    float m[3] = {0.0f, 0.0f, 0.0f};
+    for (int q = 0; q < todo; ++q) {
+      if (k_in == 0) t = 1.0;  // momentum restarts with each outer iteration
+      const double t_next = (1.0 + sqrt(1.0 + 4.0 * t * t)) / 2.0;
+      m[q] = (float)((t - 1.0) / t_next);
+      t = t_next;
+      if (++k_in == n_inner) k_in = 0;
     }
+    T *const *in = *where ? r_b : r_a;
+    T *const *out = *where ? r_a : r_b;
+    int rc;
+    if (todo == 1) {
+      rc = single(cur, in, out, m[0]);
+    } else {
+      rc = todo == 3 ? pass3(cur, alt, in, out, m[0], m[1], m[2])
+                     : pass2(cur, alt, in, out, m[0], m[1]);
+      T *const *tmp = cur;
+      cur = alt;
+      alt = tmp;
+    }
+    if (rc != 0) return TV_ERR_LAUNCH;
+    *where ^= 1;
+    s += todo;
   }
   if (cur != p) {
     for (int q = 0; q < 3; ++q)
@@ -140,6 +155,18 @@ int enqueue_pairs(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], int 
         return TV_ERR_LAUNCH;
   }
   return TV_OK;
+}
+
+// enqueue_grouped with passes of at most two steps.
+template <typename T, typename Pass, typename Single>
+int enqueue_pairs(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], int n_outer,
+                  int n_inner, size_t vol_bytes, void *stream, int *where, Pass pass,
+                  Single single) {
+  auto no_pass3 = [](T *const *, T *const *, T *const *, T *const *, float, float, float) {
+    return (int)tvfgp::kLaunchFailed;
+  };
+  return enqueue_grouped<T>(p, p_ws, r_a, r_b, n_outer, n_inner, vol_bytes, stream, where, 2,
+                            no_pass3, pass, single);
 }
 
 int enqueue_steps_tb2(const float *b, float *const p[3], float *const r_a[3],
@@ -175,6 +202,60 @@ int enqueue_steps_tb2(const float *b, float *const p[3], float *const r_a[3],
                               single);
 }
 
+int enqueue_steps_tb3(const float *b, float *const p[3], float *const r_a[3],
+                      float *const r_b[3], float lambda, float c, int n_outer,
+                      int n_inner, int64_t nx, int64_t ny, int64_t nz,
+                      float *p_ws, size_t bytes, void *stream, int *where) {
+  auto pass3 = [&](float *const *pi, float *const *po, float *const *ri, float *const *ro,
+                   float m1, float m2, float m3) {
+    tvfgp::Step3Args a;
+    a.b = b;
+    for (int q = 0; q < 3; ++q) {
+      a.p_in[q] = pi[q];
+      a.p_out[q] = po[q];
+      a.r_in[q] = ri[q];
+      a.r_out[q] = ro[q];
+    }
+    a.lam = lambda;
+    a.c = c;
+    a.m1 = m1;
+    a.m2 = m2;
+    a.m3 = m3;
+    a.nx = nx;
+    a.ny = ny;
+    a.nz = nz;
+    a.stream = stream;
+    return tvfgp::launch_tb3(a);
+  };
+  auto pass2 = [&](float *const *pi, float *const *po, float *const *ri, float *const *ro,
+                   float m1, float m2) {
+    tvfgp::Step2Args a;
+    a.b = b;
+    for (int q = 0; q < 3; ++q) {
+      a.p_in[q] = pi[q];
+      a.p_out[q] = po[q];
+      a.r_in[q] = ri[q];
+      a.r_out[q] = ro[q];
+    }
+    a.lam = lambda;
+    a.c = c;
+    a.m1 = m1;
+    a.m2 = m2;
+    a.nx = nx;
+    a.ny = ny;
+    a.nz = nz;
+    a.stream = stream;
+    return tvfgp::launch_tb2(a);
+  };
+  auto single = [&](float *const *pc, float *const *ri, float *const *ro, float m) {
+    const float *cin[3] = {ri[0], ri[1], ri[2]};
+    return tvfgp::launch_step(make_step(b, pc, cin, ro, lambda, c, m, nx, ny, nz,
+                                        tvfgp::kVariantFused, nullptr, stream));
+  };
+  return enqueue_grouped<float>(p, p_ws, r_a, r_b, n_outer, n_inner, bytes, stream, where, 3,
+                                pass3, pass2, single);
+}
+
 // Enqueue n_outer x n_inner steps; `where` (0: r_a holds r, 1: r_b) is
 // updated after every step, so the caller learns where the last r is.
 int enqueue_steps(const float *b, float *const p[3], float *const r_a[3],
@@ -183,6 +264,9 @@ int enqueue_steps(const float *b, float *const p[3], float *const r_a[3],
                   float *z_ws, void *stream, int *where) {
   if (variant == tvfgp::kVariantTb2)
     return enqueue_steps_tb2(b, p, r_a, r_b, lambda, c, n_outer, n_inner, nx, ny, nz, z_ws,
+                             volume_bytes(nx, ny, nz), stream, where);
+  if (variant == tvfgp::kVariantTb3)
+    return enqueue_steps_tb3(b, p, r_a, r_b, lambda, c, n_outer, n_inner, nx, ny, nz, z_ws,
                              volume_bytes(nx, ny, nz), stream, where);
   for (int o = 0; o < n_outer; ++o) {
     double t = 1.0;
@@ -207,7 +291,7 @@ int enqueue_steps(const float *b, float *const p[3], float *const r_a[3],
 // variant's z, the two-steps-per-pass variant's second p (three volumes).
 size_t run_workspace_bytes(int variant, size_t bytes) {
   if (variant == tvfgp::kVariantTwoKernel) return bytes;
-  if (variant == tvfgp::kVariantTb2) return 3 * bytes;
+  if (variant == tvfgp::kVariantTb2 || variant == tvfgp::kVariantTb3) return 3 * bytes;
   return 0;
 }
 
@@ -342,6 +426,47 @@ int tv_fgp_step2(const float *b, const float *const p_in[3], float *const p_out[
   a.nz = nz;
   a.stream = stream;
   return launch_status(tvfgp::launch_tb2(a));
+}
+
+int tv_fgp_step3(const float *b, const float *const p_in[3], float *const p_out[3],
+                 const float *const r_in[3], float *const r_out[3], float lambda,
+                 float m1, float m2, float m3, int64_t nx, int64_t ny, int64_t nz,
+                 void *stream) {
+  if (p_in == nullptr || p_out == nullptr || r_in == nullptr || r_out == nullptr)
+    return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  if (!isfinite(m1) || !isfinite(m2) || !isfinite(m3)) return TV_ERR_PARAM;
+  const Buf bufs[13] = {vol(b, bytes, false),        vol(p_in[0], bytes, false),
+                        vol(p_in[1], bytes, false),  vol(p_in[2], bytes, false),
+                        vol(p_out[0], bytes, true),  vol(p_out[1], bytes, true),
+                        vol(p_out[2], bytes, true),  vol(r_in[0], bytes, false),
+                        vol(r_in[1], bytes, false),  vol(r_in[2], bytes, false),
+                        vol(r_out[0], bytes, true),  vol(r_out[1], bytes, true),
+                        vol(r_out[2], bytes, true)};
+  st = check_buffers(bufs, 13);
+  if (st != TV_OK) return st;
+  tvfgp::Step3Args a;
+  a.b = b;
+  for (int q = 0; q < 3; ++q) {
+    a.p_in[q] = p_in[q];
+    a.p_out[q] = p_out[q];
+    a.r_in[q] = r_in[q];
+    a.r_out[q] = r_out[q];
+  }
+  a.lam = lambda;
+  a.c = c;
+  a.m1 = m1;
+  a.m2 = m2;
+  a.m3 = m3;
+  a.nx = nx;
+  a.ny = ny;
+  a.nz = nz;
+  a.stream = stream;
+  return launch_status(tvfgp::launch_tb3(a));
 }
 
 int tv_primal(const float *b, const float *const p[3], float *z, float lambda,
@@ -729,6 +854,7 @@ const char *tv_fgp_variant_name(int variant) {
     case tvfgp::kVariantRegMarch: return "reg_march";
     case tvfgp::kVariantPair: return "pair";
     case tvfgp::kVariantTb2: return "tb2";
+    case tvfgp::kVariantTb3: return "tb3";
     case tvfgp::kVariantCube: return "cube";
     case tvfgp::kVariantCube32x8x2: return "cube_32x8x2";
     case tvfgp::kVariantCube64x8x1: return "cube_64x8x1";

@@ -48,6 +48,7 @@ int launch_step_t(const StepArgs &a) {
     case kVariantPair:
       return launch_fused_pair(a);
     case kVariantTb2:  // a single step: the fused kernel
+    case kVariantTb3:
       return launch_fused_zx(a);
     case kVariantCube:
     case kVariantCube32x8x2:

@@ -20,7 +20,8 @@ constexpr int kVariantCube32x8x2 = 8;
 constexpr int kVariantCube64x8x1 = 9;
 constexpr int kVariantCube8x8x8 = 10;
 constexpr int kVariantCube32x4x4 = 11;
-constexpr int kNumVariants = 12;
+constexpr int kVariantTb3 = 12;
+constexpr int kNumVariants = 13;
 
 constexpr int kLaunchFailed = -1;
 
@@ -64,6 +65,19 @@ struct Step2ArgsH {
   const uint16_t *r_in[3];
   uint16_t *r_out[3];
   float lam, c, m1, m2;
+  int64_t nx, ny, nz;
+  void *stream;
+};
+
+// Three steps in one pass: p_in -> p_out (separate buffers), r_in -> r_out,
+// momentum m1, m2, m3 for the three steps.
+struct Step3Args {
+  const float *b;
+  const float *p_in[3];
+  float *p_out[3];
+  const float *r_in[3];
+  float *r_out[3];
+  float lam, c, m1, m2, m3;
   int64_t nx, ny, nz;
   void *stream;
 };
@@ -122,6 +136,7 @@ int launch_fused_pair(const StepArgs &a);
 int launch_fused_pair_h(const StepArgsH &a);
 int launch_tb2(const Step2Args &a);
 int launch_tb2_h(const Step2ArgsH &a);
+int launch_tb3(const Step3Args &a);
 // Cube-tiled ablation, shape chosen by a.variant (kVariantCube...).
 int launch_cube(const StepArgs &a);
 int launch_primal_h(const PrimalArgsH &a);

@@ -1,0 +1,332 @@
+// Three FGP steps in one pass over HBM (temporal blocking along the z march,
+// one level deeper than tv_fgp_tb2_kernel.hpp).
+//
+// One step ("TV solver: the FGP step on the GPU", section "What one step
+// does") makes the new r at a voxel depend on the old r within one voxel of
+// it, so three steps depend on the old r within three.  A workgroup owns a
+// 64 x 8 (x, y) tile and a slab of planes; it runs step one on the tile grown
+// by two voxels in x and y, step two on the tile grown by one, step three on
+// the tile, keeping the intermediate p and r on chip: b, p and r are read
+// once and p, r written once per three steps.
+//
+// Every value is computed by the same device functions in the same order as
+// the one-step kernels (primal_z, dual_update), so three launches of those and
+// one launch of this give the same bits; with binary16 storage the p and r of
+// steps one and two are rounded as a stored step rounds them.
+//
+// Regions in tile coordinates (x, y), the tile being T = [0, 64) x [0, 8):
+//   R0 = [-2, 66] x [-2, 10]  primal z0 of the input r     69 x 13
+//   E1 = [-2, 65] x [-2,  9]  step one  -> p1, r1          68 x 12
+//   R1 = [-1, 65] x [-1,  9]  primal z1 of r1              67 x 11
+//   E2 = [-1, 64] x [-1,  8]  step two  -> p2, r2          66 x 10
+//   R2 = [ 0, 64] x [ 0,  8]  primal z2 of r2              65 x  9
+// Thread t owns tile point (t % 64, t / 64); threads 0..384 also own one of
+// the 385 points of R0 outside the tile.
+//
+// Iteration k of the z march (k from z0 - 7 to z1 - 1 for the slab [z0, z1)):
+//   phase 1: z2 at plane k+1 on R2, z1 at plane k+3 on R1, z0 at plane k+5
+//            on R0 (from the loads of plane k+5)
+//   barrier
+//   phase 2: step three at plane k on T -> p_out, r_out;
+//            step two at plane k+2 on E2 -> r2 into LDS, p2 and r2 kept;
+//            step one at plane k+4 on E1 -> r1 into LDS, p1 and r1 kept
+//   barrier
+// LDS rings of two planes hold z0, z1, z2 and the z components of r1 and r2;
+// their x and y components need one plane.  Each slot is rewritten only after
+// the barrier that follows its last read.  The input p is read at halo points
+// of neighbouring tiles, so the new p goes to a second buffer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <stdint.h>
+
+#include "tv_fgp_device.hpp"
+#include "tv_fgp_fused_kernel.hpp"
+#include "tv_fgp_tb2_kernel.hpp"
+
+#pragma clang fp contract(off)
+
+namespace tvfgp {
+
+constexpr int kT3R0X = kTbTileX + 5, kT3R0Y = kTbTileY + 5;  // 69 x 13
+constexpr int kT3E1X = kTbTileX + 4, kT3E1Y = kTbTileY + 4;  // 68 x 12
+constexpr int kT3R1X = kTbTileX + 3, kT3R1Y = kTbTileY + 3;  // 67 x 11
+constexpr int kT3E2X = kTbTileX + 2, kT3E2Y = kTbTileY + 2;  // 66 x 10
+constexpr int kT3R2X = kTbTileX + 1, kT3R2Y = kTbTileY + 1;  // 65 x  9
+constexpr int kT3Halo = kT3R0X * kT3R0Y - kTbTileX * kTbTileY;  // 385
+
+// Tile coordinates of the h-th R0 point outside the tile: the rows y = -2,
+// -1, 8, 9, 10 (x = -2..66), then the columns x = -2, -1, 64, 65, 66
+// (y = 0..7).
+__device__ __forceinline__ void tb3_halo_point(int h, int &x, int &y) {
+  if (h < 5 * kT3R0X) {
+    const int row = h / kT3R0X;
+    y = row < 2 ? row - 2 : kTbTileY + row - 2;
+    x = h % kT3R0X - 2;
+  } else {
+    const int c = h - 5 * kT3R0X;
+    const int col = c / kTbTileY;
+    y = c % kTbTileY;
+    x = col < 2 ? col - 2 : kTbTileX + col - 2;
+  }
+}
+
+// Region membership of a point and the state it carries beyond TbPoint.
+struct Tb3Extra {
+  bool e1, r1, e2, r2;
+  float b2, b1;                        // b of planes k+2 and k+1
+  float p1a0, p1a1, p1a2, r1a0, r1a1, r1a2;  // step one's p1, r1 of plane k+2
+  float p1b0, p1b1, p1b2, r1b0, r1b1, r1b2;  // ... of plane k+3
+};
+
+__device__ __forceinline__ void tb3_init_extra(Tb3Extra &e, int lx, int ly) {
+  e.e1 = lx >= -2 && lx <= kTbTileX + 1 && ly >= -2 && ly <= kTbTileY + 1;
+  e.r1 = lx >= -1 && lx <= kTbTileX + 1 && ly >= -1 && ly <= kTbTileY + 1;
+  e.e2 = lx >= -1 && lx <= kTbTileX && ly >= -1 && ly <= kTbTileY;
+  e.r2 = lx >= 0 && lx <= kTbTileX && ly >= 0 && ly <= kTbTileY;
+  e.b2 = e.b1 = 0.0f;
+  e.p1a0 = e.p1a1 = e.p1a2 = e.r1a0 = e.r1a1 = e.r1a2 = 0.0f;
+  e.p1b0 = e.p1b1 = e.p1b2 = e.r1b0 = e.r1b1 = e.r1b2 = 0.0f;
+}
+
+// Four waves per SIMD: the carried state of three levels needs ~100 VGPRs.
+template <typename I, typename Off, typename S>
+__global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
+    const float *__restrict__ b, const S *__restrict__ pi0,
+    const S *__restrict__ pi1, const S *__restrict__ pi2,
+    S *__restrict__ po0, S *__restrict__ po1, S *__restrict__ po2,
+    const S *__restrict__ ri0, const S *__restrict__ ri1,
+    const S *__restrict__ ri2, S *__restrict__ ro0, S *__restrict__ ro1,
+    S *__restrict__ ro2, float lam, float c, float m1, float m2, float m3,
+    ZxGeometry<I, Off> g) {
+  __shared__ float z0r[2][kT3R0Y][kT3R0X];    // z0 at (x+2, y+2)
+  __shared__ float r1x[kT3E1Y][kT3E1X];       // r1_x at (x+2, y+2)
+  __shared__ float r1y[kT3E1Y][kT3E1X];       // r1_y
+  __shared__ float r1z[2][kT3E1Y][kT3E1X];    // r1_z, two planes
+  __shared__ float z1r[2][kT3R1Y][kT3R1X];    // z1 at (x+1, y+1)
+  __shared__ float r2x[kT3E2Y][kT3E2X];       // r2_x at (x+1, y+1)
+  __shared__ float r2y[kT3E2Y][kT3E2X];       // r2_y
+  __shared__ float r2z[2][kT3E2Y][kT3E2X];    // r2_z, two planes
+  __shared__ float z2r[2][kT3R2Y][kT3R2X];    // z2 at (x, y)
+  const int tid = (int)threadIdx.x;
+  const bool has_halo = tid < kT3Halo;
+  int hlx = 0, hly = 0;
+  if (has_halo) tb3_halo_point(tid, hlx, hly);
+  const Off sy4 = g.sy4, sz4 = g.sz4;
+
+  for (I t = (I)blockIdx.x; t < g.ntiles; t += (I)gridDim.x) {
+    I tx, ty, tz;
+    ordered_tile<I, Off>(xcd_tile(t, g.ntiles), g, tx, ty, tz);
+    const I x0 = tx * kTbTileX, y0 = ty * kTbTileY;
+    const I z0 = tz * g.planes;
+    const I z1 = (z0 + g.planes < g.nz) ? z0 + g.planes : g.nz;
+    TbPoint<Off> own, hal;
+    tb_init_point<I, Off>(own, tid % kTbTileX, tid / kTbTileX, x0, y0, g);
+    tb_init_point<I, Off>(hal, hlx, hly, x0, y0, g);
+    hal.ok = hal.ok && has_halo;
+    Tb3Extra ox, hx;
+    tb3_init_extra(ox, own.lx, own.ly);
+    tb3_init_extra(hx, hal.lx, hal.ly);
+    // own p2, r2 of planes k and k+1 (step two at the thread's tile point)
+    float pa0 = 0.0f, pa1 = 0.0f, pa2 = 0.0f, ra0 = 0.0f, ra1 = 0.0f, ra2 = 0.0f;
+    float pb0 = 0.0f, pb1 = 0.0f, pb2 = 0.0f, rb0 = 0.0f, rb1 = 0.0f, rb2 = 0.0f;
+
+    const I kstart = z0 - 7;
+    // planes whose inputs the slab reads: [z0 - 2, z1 + 2] (and r_z of z0 - 3)
+    const I lo_in = z0 - 2, hi_in = z1 + 2;
+    auto input_plane = [&](I kp) { return kp >= 0 && kp < g.nz && kp >= lo_in && kp <= hi_in; };
+    if (z0 - 3 >= 0) {
+      const Off j = (Off)(z0 - 3) * sz4;
+      own.q2 = lds(ri2, own.o + j);
+      if (has_halo) hal.q2 = lds(ri2, hal.o + j);
+    }
+    if (input_plane(z0 - 2)) {
+      tb_load<S, Off>(own, (Off)(z0 - 2) * sz4, sy4, b, ri0, ri1, ri2);
+      if (has_halo) tb_load<S, Off>(hal, (Off)(z0 - 2) * sz4, sy4, b, ri0, ri1, ri2);
+    }
+    tb_take(own);
+    tb_take(hal);
+
+    for (I k = kstart; k < z1; ++k) {
+      const I kd1 = k + 4;  // step-one plane
+      const bool do_d1 = kd1 >= z0 - 2 && kd1 >= 0 && kd1 < g.nz && kd1 <= z1 + 1;
+      const I kd2 = k + 2;  // step-two plane
+      const bool do_d2 = kd2 >= z0 - 1 && kd2 >= 0 && kd2 < g.nz && kd2 <= z1;
+      const I kb = k + 5;   // z0 plane
+      const bool do_b = input_plane(kb);
+      const I kf1 = k + 3;  // z1 plane
+      const bool do_f1 = kf1 >= z0 - 1 && kf1 >= 0 && kf1 < g.nz && kf1 <= z1 + 1;
+      const I kf2 = k + 1;  // z2 plane
+      const bool do_f2 = kf2 >= z0 && kf2 < g.nz && kf2 <= z1;
+      const bool do_h = k >= z0;
+      // p_in of the step-one plane
+      if (do_d1) {
+        const Off j = (Off)kd1 * sz4;
+        own.pp0 = lds(pi0, own.o + j);
+        own.pp1 = lds(pi1, own.o + j);
+        own.pp2 = lds(pi2, own.o + j);
+        if (has_halo) {
+          hal.pp0 = lds(pi0, hal.o + j);
+          hal.pp1 = lds(pi1, hal.o + j);
+          hal.pp2 = lds(pi2, hal.o + j);
+        }
+      }
+      // inputs of plane k+6, consumed next iteration
+      const I kl = k + 6;
+      if (input_plane(kl)) {
+        tb_load<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+        if (has_halo) tb_load<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+      }
+
+      // ---- phase 1: z2 of plane k+1 on R2, z1 of plane k+3 on R1, z0 of
+      // plane k+5 on R0.  Every index is inside its array (the lower
+      // neighbours of R2 lie in E2, those of R1 in E1), so the reads are
+      // unconditional and the boundary rule is a select.
+      auto phase_f2 = [&](TbPoint<Off> &pt, const Tb3Extra &e) {
+        const int x = pt.lx + 1, y = pt.ly + 1;
+        const int s = (int)(kf2 & 1), sp = (int)((kf2 + 1) & 1);
+        const float rx = r2x[y][x], ry = r2y[y][x], rz = r2z[s][y][x];
+        const float rxm = r2x[y][x - 1], rym = r2y[y - 1][x], rzm = r2z[sp][y][x];
+        z2r[s][pt.ly][pt.lx] = primal_z(e.b1, rx, pt.low_x ? rxm : 0.0f, ry,
+                                        pt.low_y ? rym : 0.0f, rz, kf2 > 0 ? rzm : 0.0f, lam);
+      };
+      auto phase_f1 = [&](TbPoint<Off> &pt) {
+        const int x = pt.lx + 2, y = pt.ly + 2;
+        const int s = (int)(kf1 & 1), sp = (int)((kf1 + 1) & 1);
+        const float rx = r1x[y][x], ry = r1y[y][x], rz = r1z[s][y][x];
+        const float rxm = r1x[y][x - 1], rym = r1y[y - 1][x], rzm = r1z[sp][y][x];
+        z1r[s][pt.ly + 1][pt.lx + 1] =
+            primal_z(pt.bqq, rx, pt.low_x ? rxm : 0.0f, ry, pt.low_y ? rym : 0.0f, rz,
+                     kf1 > 0 ? rzm : 0.0f, lam);
+      };
+      auto phase_b = [&](TbPoint<Off> &pt) {
+        z0r[kb & 1][pt.ly + 2][pt.lx + 2] =
+            primal_z(pt.cb, pt.c0, pt.low_x ? pt.c0l : 0.0f, pt.c1,
+                     pt.low_y ? pt.c1l : 0.0f, pt.c2, kb > 0 ? pt.q2 : 0.0f, lam);
+      };
+      if (do_f2) {
+        if (own.ok) phase_f2(own, ox);
+        if (hal.ok && hx.r2) phase_f2(hal, hx);
+      }
+      if (do_f1) {
+        if (own.ok) phase_f1(own);
+        if (hal.ok && hx.r1) phase_f1(hal);
+      }
+      if (do_b) {
+        if (own.ok) phase_b(own);
+        if (hal.ok) phase_b(hal);
+      }
+      __syncthreads();
+
+      // ---- phase 2: step three at plane k (tile), step two at plane k+2
+      // (E2), step one at plane k+4 (E1)
+      if (do_h && own.ok) {
+        const int s = (int)(k & 1), sn = (int)((k + 1) & 1);
+        const int x = own.lx, y = own.ly;
+        const float zi = z2r[s][y][x], zx = z2r[s][y][x + 1], zy = z2r[s][y + 1][x];
+        const float zz = z2r[sn][y][x];
+        float o0, o1, o2;
+        dual_update(zi, zx, zy, zz, own.has_x, own.has_y, k + 1 < g.nz, ra0, ra1, ra2,
+                    pa0, pa1, pa2, c, m3, o0, o1, o2);
+        const Off j = own.o + (Off)k * sz4;
+        sts_stream(po0, j, pa0);
+        sts_stream(po1, j, pa1);
+        sts_stream(po2, j, pa2);
+        sts_stream(ro0, j, o0);
+        sts_stream(ro1, j, o1);
+        sts_stream(ro2, j, o2);
+      }
+      pa0 = pb0;
+      pa1 = pb1;
+      pa2 = pb2;
+      ra0 = rb0;
+      ra1 = rb1;
+      ra2 = rb2;
+      // step two at an E2 point from its step-one p1, r1 of plane k+2
+      auto phase_d2 = [&](TbPoint<Off> &pt, Tb3Extra &e, float &p0o, float &p1o, float &p2o,
+                          float &r0o, float &r1o, float &r2o) {
+        const int x = pt.lx + 1, y = pt.ly + 1;
+        const int s = (int)(kd2 & 1), sn = (int)((kd2 + 1) & 1);
+        const float zi = z1r[s][y][x], zx = z1r[s][y][x + 1], zy = z1r[s][y + 1][x];
+        const float zz = z1r[sn][y][x];
+        p0o = e.p1a0;
+        p1o = e.p1a1;
+        p2o = e.p1a2;
+        dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd2 + 1 < g.nz, e.r1a0, e.r1a1,
+                    e.r1a2, p0o, p1o, p2o, c, m2, r0o, r1o, r2o);
+        p0o = as_stored<S>(p0o);
+        p1o = as_stored<S>(p1o);
+        p2o = as_stored<S>(p2o);
+        r0o = as_stored<S>(r0o);
+        r1o = as_stored<S>(r1o);
+        r2o = as_stored<S>(r2o);
+        r2x[y][x] = r0o;
+        r2y[y][x] = r1o;
+        r2z[s][y][x] = r2o;
+      };
+      if (do_d2) {
+        if (own.ok) phase_d2(own, ox, pb0, pb1, pb2, rb0, rb1, rb2);
+        if (hal.ok && hx.e2) {
+          float q0, q1, q2, s0, s1, s2;
+          phase_d2(hal, hx, q0, q1, q2, s0, s1, s2);
+        }
+      }
+      auto shift1 = [](Tb3Extra &e) {
+        e.p1a0 = e.p1b0;
+        e.p1a1 = e.p1b1;
+        e.p1a2 = e.p1b2;
+        e.r1a0 = e.r1b0;
+        e.r1a1 = e.r1b1;
+        e.r1a2 = e.r1b2;
+      };
+      shift1(ox);
+      shift1(hx);
+      // step one at an E1 point from the input r and p of plane k+4
+      auto phase_d1 = [&](TbPoint<Off> &pt, Tb3Extra &e) {
+        const int x = pt.lx + 2, y = pt.ly + 2;
+        const int s = (int)(kd1 & 1), sn = (int)((kd1 + 1) & 1);
+        const float zi = z0r[s][y][x], zx = z0r[s][y][x + 1], zy = z0r[s][y + 1][x];
+        const float zz = z0r[sn][y][x];
+        float r0o, r1o, r2o;
+        dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd1 + 1 < g.nz, pt.q0, pt.q1, pt.q2,
+                    pt.pp0, pt.pp1, pt.pp2, c, m1, r0o, r1o, r2o);
+        e.p1b0 = as_stored<S>(pt.pp0);
+        e.p1b1 = as_stored<S>(pt.pp1);
+        e.p1b2 = as_stored<S>(pt.pp2);
+        e.r1b0 = as_stored<S>(r0o);
+        e.r1b1 = as_stored<S>(r1o);
+        e.r1b2 = as_stored<S>(r2o);
+        r1x[y][x] = e.r1b0;
+        r1y[y][x] = e.r1b1;
+        r1z[s][y][x] = e.r1b2;
+      };
+      if (do_d1) {
+        if (own.ok) phase_d1(own, ox);
+        if (hal.ok && hx.e1) phase_d1(hal, hx);
+      }
+      __syncthreads();
+      ox.b1 = ox.b2;
+      ox.b2 = own.bqq;
+      hx.b1 = hx.b2;
+      hx.b2 = hal.bqq;
+      tb_rotate(own);
+      tb_rotate(hal);
+    }
+  }
+}
+
+// Planes per slab: the largest of 96, 64, 32 and 16 that still gives at
+// least 1024 tiles (two per workgroup slot at two workgroups per CU), else 8.
+// A slab re-reads 6 planes and runs 7 pipeline-filling iterations, so long
+// slabs pay off; at 512^3, 16 / 32 / 48 / 64 / 96 / 128 planes measured
+// 0.776 / 0.734 / 0.727 / 0.723 / 0.716 / 0.722 ms per step of a 20 x 10 run.
+inline int64_t tb3_planes(int64_t nx, int64_t ny, int64_t nz) {
+  const int64_t txy = ((nx + kTbTileX - 1) / kTbTileX) * ((ny + kTbTileY - 1) / kTbTileY);
+  const int64_t choices[4] = {96, 64, 32, 16};
+  for (int i = 0; i < 4; ++i)
+    if (txy * ((nz + choices[i] - 1) / choices[i]) >= 1024) return choices[i];
+  return 8;
+}
+
+}  // namespace tvfgp

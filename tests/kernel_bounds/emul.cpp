@@ -29,6 +29,7 @@
 #include "tv_fgp_lds_kernel.hpp"
 #include "tv_fgp_pair_kernel.hpp"
 #include "tv_fgp_tb2_kernel.hpp"
+#include "tv_fgp_tb3_kernel.hpp"
 #include "tv_fgp_cube_kernel.hpp"
 
 thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
@@ -82,6 +83,22 @@ unsigned pick_grid(int64_t ntiles, unsigned override_grid) {
 struct Bufs {
   float *b, *p[3], *ri[3], *ro[3], *z, *po[3];
 };
+
+template <typename I, typename Off, typename S>
+void run_tb3(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid, int64_t planes) {
+  const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz, planes);
+  S *p[3], *po[3], *ri[3], *ro[3];
+  for (int a = 0; a < 3; ++a) {
+    p[a] = (S *)v.p[a];
+    po[a] = (S *)v.po[a];
+    ri[a] = (S *)v.ri[a];
+    ro[a] = (S *)v.ro[a];
+  }
+  run_grid(pick_grid(g.ntiles, grid), tvfgp::kTbBlock, [&] {
+    tvfgp::tb3_kernel<I, Off, S>(v.b, p[0], p[1], p[2], po[0], po[1], po[2], ri[0], ri[1], ri[2],
+                                 ro[0], ro[1], ro[2], 0.01f, 8.3f, 0.3f, 0.5f, 0.6f, g);
+  });
+}
 
 template <typename I, typename Off, typename S>
 void run_tb2(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid, int64_t planes) {
@@ -262,6 +279,18 @@ int main(int argc, char **argv) {
       run_fused<int64_t, uint64_t, float>(v, nx, ny, nz, grid, sp);
     else
       run_fused<int32_t, uint32_t, float>(v, nx, ny, nz, grid, sp);
+  } else if (!strcmp(variant, "tb3") || !strcmp(variant, "tb3_h")) {
+    if (half) {
+      if (wide)
+        run_tb3<int64_t, uint64_t, _Float16>(v, nx, ny, nz, grid, planes);
+      else
+        run_tb3<int32_t, uint32_t, _Float16>(v, nx, ny, nz, grid, planes);
+    } else {
+      if (wide)
+        run_tb3<int64_t, uint64_t, float>(v, nx, ny, nz, grid, planes);
+      else
+        run_tb3<int32_t, uint32_t, float>(v, nx, ny, nz, grid, planes);
+    }
   } else if (!strcmp(variant, "tb2") || !strcmp(variant, "tb2_h")) {
     if (half) {
       if (wide)

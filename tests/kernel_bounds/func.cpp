@@ -19,6 +19,7 @@
 //           tb2    two steps (m1 then m2) in one pass, p_in -> p_out
 //           tb2_h  the same with p and r stored as binary16 (files hold the
 //                  binary16 values as floats)
+//           tb3, tb3_h  three steps (m1, m2, m3) in one pass
 //   dir holds b.bin (n floats), p.bin and r.bin (3n floats each); the kernel
 //   writes p_out.bin and r_out.bin there.
 #include <condition_variable>
@@ -32,6 +33,7 @@
 
 #include "tv_fgp_fused_kernel.hpp"
 #include "tv_fgp_tb2_kernel.hpp"
+#include "tv_fgp_tb3_kernel.hpp"
 #include "tv_fgp_cube_kernel.hpp"
 #include "tv_fgp_lds_kernel.hpp"
 #include "tv_fgp_gap_kernel.hpp"
@@ -111,6 +113,7 @@ unsigned pick(int64_t ntiles, unsigned grid) {
 
 template <typename I, typename Off>
 void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, float m1, float m2,
+         float m3,
          unsigned grid, const float *b, float *p, float *r, float *p_out, float *r_out,
          const std::string &dir, int64_t planes) {
   const size_t n = (size_t)(nx * ny * nz);
@@ -208,6 +211,32 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
                                      r_out + n, r_out + 2 * n, lam, c, m1, g);
     });
     memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "tb3")) {
+    const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz,
+                                              planes > 0 ? planes : tvfgp::tb3_planes(nx, ny, nz));
+    run_grid(pick(g.ntiles, grid), tvfgp::kTbBlock, [&] {
+      tvfgp::tb3_kernel<I, Off, float>(b, p, p + n, p + 2 * n, p_out, p_out + n, p_out + 2 * n,
+                                       r, r + n, r + 2 * n, r_out, r_out + n, r_out + 2 * n, lam,
+                                       c, m1, m2, m3, g);
+    });
+  } else if (!strcmp(kernel, "tb3_h")) {
+    typedef _Float16 h;
+    std::vector<h> ph(3 * n), rh(3 * n), poh(3 * n), roh(3 * n);
+    for (size_t i = 0; i < 3 * n; ++i) {
+      ph[i] = (h)p[i];
+      rh[i] = (h)r[i];
+    }
+    const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz,
+                                              planes > 0 ? planes : tvfgp::tb3_planes(nx, ny, nz));
+    h *P = ph.data(), *R = rh.data(), *PO = poh.data(), *RO = roh.data();
+    run_grid(pick(g.ntiles, grid), tvfgp::kTbBlock, [&] {
+      tvfgp::tb3_kernel<I, Off, h>(b, P, P + n, P + 2 * n, PO, PO + n, PO + 2 * n, R, R + n,
+                                   R + 2 * n, RO, RO + n, RO + 2 * n, lam, c, m1, m2, m3, g);
+    });
+    for (size_t i = 0; i < 3 * n; ++i) {
+      p_out[i] = (float)poh[i];
+      r_out[i] = (float)roh[i];
+    }
   } else if (!strcmp(kernel, "tb2")) {
     const auto g = tvfgp::tb_geometry<I, Off>(nx, ny, nz, planes);
     run_grid(pick(g.ntiles, grid), tvfgp::kTbBlock, [&] {
@@ -242,11 +271,12 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
 }  // namespace
 
 int main(int argc, char **argv) {
-  if (argc != 11 && argc != 12) {
-    fprintf(stderr, "usage: func kernel nx ny nz lambda m1 m2 dir wide grid [planes]\n");
+  if (argc < 11 || argc > 13) {
+    fprintf(stderr, "usage: func kernel nx ny nz lambda m1 m2 dir wide grid [planes [m3]]\n");
     return 2;
   }
-  const int64_t planes = argc == 12 ? atoll(argv[11]) : 0;
+  const int64_t planes = argc >= 12 ? atoll(argv[11]) : 0;
+  const float m3 = argc == 13 ? strtof(argv[12], nullptr) : 0.0f;
   const char *kernel = argv[1];
   const int64_t nx = atoll(argv[2]), ny = atoll(argv[3]), nz = atoll(argv[4]);
   const float lam = strtof(argv[5], nullptr), m1 = strtof(argv[6], nullptr),
@@ -260,10 +290,10 @@ int main(int argc, char **argv) {
   std::vector<float> r = read_file(dir + "/r.bin", 3 * n);
   std::vector<float> p_out(3 * n, -12345.0f), r_out(3 * n, -12345.0f);
   if (wide)
-    run<int64_t, uint64_t>(kernel, nx, ny, nz, lam, m1, m2, grid, b.data(), p.data(),
+    run<int64_t, uint64_t>(kernel, nx, ny, nz, lam, m1, m2, m3, grid, b.data(), p.data(),
                            r.data(), p_out.data(), r_out.data(), dir, planes);
   else
-    run<int32_t, uint32_t>(kernel, nx, ny, nz, lam, m1, m2, grid, b.data(), p.data(),
+    run<int32_t, uint32_t>(kernel, nx, ny, nz, lam, m1, m2, m3, grid, b.data(), p.data(),
                            r.data(), p_out.data(), r_out.data(), dir, planes);
   write_file(dir + "/p_out.bin", p_out);
   write_file(dir + "/r_out.bin", r_out);

@@ -42,7 +42,7 @@ def test_c_program_builds(tmp_path):
 
 
 @pytest.mark.gpu
-@pytest.mark.parametrize("variant", [0, 6], ids=["fused", "tb2"])
+@pytest.mark.parametrize("variant", [0, 6, 12], ids=["fused", "tb2", "tb3"])
 def test_c_program_matches_oracle(tmp_path, variant):
     exe = build(str(tmp_path / "fgp_abi_c"))
     dims = (67, 45, 29)

@@ -81,7 +81,8 @@ def test_status_strings_distinct():
 def test_variant_names():
     for name, v in tvf.VARIANTS.items():
         assert tvf.variant_name(v) == name
-    assert tvf.variant_name(12) is None
+    assert tvf.variant_name(13) is None
+    assert tvf.variant_name(-1) is None
 
 
 def test_workspace_bytes():
@@ -90,8 +91,9 @@ def test_workspace_bytes():
         assert tvf.workspace_bytes(v, 10, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.TWO_KERNEL, 0, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.TB2, 10, 20, 30) == 3 * 10 * 20 * 30 * 4
+    assert tvf.workspace_bytes(tvf.TB3, 10, 20, 30) == 3 * 10 * 20 * 30 * 4
     assert tvf.workspace_bytes(tvf.PAIR, 10, 20, 30) == 0
-    assert tvf.workspace_bytes(12, 10, 20, 30) == 0
+    assert tvf.workspace_bytes(13, 10, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.CUBE, 10, 20, 30) == 0
     assert tvf.workspace_bytes(tvf.TWO_KERNEL, 1 << 31, 1 << 31, 1 << 31) == 0
 
@@ -120,7 +122,7 @@ def test_workspace_bytes():
     (dict(lam=1e-45), tvf.TV_ERR_PARAM),           # 1/(12 lambda) overflows
     (dict(m=float("nan")), tvf.TV_ERR_PARAM),
     (dict(m=float("inf")), tvf.TV_ERR_PARAM),
-    (dict(variant=12), tvf.TV_ERR_VARIANT),
+    (dict(variant=13), tvf.TV_ERR_VARIANT),
     (dict(variant=-1), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),       # two-kernel without z
     (dict(variant=2, ws=0), tvf.TV_ERR_ALIAS),     # workspace aliases b
@@ -170,7 +172,7 @@ def run(b=0, p=(1, 2, 3), ra=(4, 5, 6), rb=(7, 8, 9), lam=0.01, n_outer=2, n_inn
     (dict(rb=(7, 8, 4)), tvf.TV_ERR_ALIAS),        # r_b aliases r_a
     (dict(ra=(4, 5, 1)), tvf.TV_ERR_ALIAS),        # r_a aliases p
     (dict(dims=(NX, NY, -4)), tvf.TV_ERR_DIMS),
-    (dict(variant=12), tvf.TV_ERR_VARIANT),
+    (dict(variant=13), tvf.TV_ERR_VARIANT),
     (dict(variant=2), tvf.TV_ERR_WORKSPACE),
     (dict(variant=6), tvf.TV_ERR_WORKSPACE),       # two steps per pass without p workspace
     (dict(variant=6, ws=9), tvf.TV_ERR_ALIAS),     # first workspace volume is r_b[2]
@@ -314,19 +316,23 @@ def test_primal_h_rejects():
         == tvf.TV_ERR_NULL
 
 
-def test_run_tb2_accepts_three_volume_workspace():
+@pytest.mark.parametrize("variant", [tvf.TB2, tvf.TB3], ids=["tb2", "tb3"])
+def test_run_multistep_accepts_three_volume_workspace(variant):
     # nothing is enqueued with n_outer = 0, so the checks alone decide
-    st, where = run(variant=tvf.TB2, ws=10, n_outer=0)
+    st, where = run(variant=variant, ws=10, n_outer=0)
     assert st == tvf.TV_OK and where == 0
+    st, _ = run(variant=variant, ws=None, n_outer=0)
+    assert st == tvf.TV_ERR_WORKSPACE
 
 
-def test_run_tb2_workspace_spans_three_volumes():
+@pytest.mark.parametrize("variant", [tvf.TB2, tvf.TB3], ids=["tb2", "tb3"])
+def test_run_multistep_workspace_spans_three_volumes(variant):
     # b placed inside the third volume of the workspace overlaps it; just past it, not
     ws = addr(10)
     for b_addr, code in ((ws + 2 * VOL + 4, tvf.TV_ERR_ALIAS), (ws + 3 * VOL, tvf.TV_OK)):
         where = ctypes.c_int(-7)
         st = L.tv_fgp_run(b_addr, field(1, 2, 3), field(4, 5, 6), field(7, 8, 9), 0.01, 0, 3,
-                          NX, NY, NZ, tvf.TB2, ws, None, ctypes.byref(where))
+                          NX, NY, NZ, variant, ws, None, ctypes.byref(where))
         assert st == code
 
 
@@ -350,6 +356,29 @@ def step2(b=0, pi=(1, 2, 3), po=(10, 11, 12), ri=(4, 5, 6), ro=(7, 8, 9), lam=0.
 ])
 def test_step2_rejects(kw, code):
     assert step2(**kw) == code
+
+
+def step3(b=0, pi=(1, 2, 3), po=(10, 11, 12), ri=(4, 5, 6), ro=(7, 8, 9), lam=0.01, m1=0.0,
+          m2=0.3, m3=0.4, dims=(NX, NY, NZ)):
+    return L.tv_fgp_step3(None if b is None else addr(b), field(*pi), field(*po), field(*ri),
+                          field(*ro), lam, m1, m2, m3, *dims, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=None), tvf.TV_ERR_NULL),
+    (dict(pi=(1, None, 3)), tvf.TV_ERR_NULL),
+    (dict(dims=(NX, NY, 0)), tvf.TV_ERR_DIMS),
+    (dict(lam=float("nan")), tvf.TV_ERR_PARAM),
+    (dict(m1=float("inf")), tvf.TV_ERR_PARAM),
+    (dict(m2=float("nan")), tvf.TV_ERR_PARAM),
+    (dict(m3=float("-inf")), tvf.TV_ERR_PARAM),
+    (dict(po=(1, 11, 12)), tvf.TV_ERR_ALIAS),   # p_out on p_in
+    (dict(po=(10, 5, 12)), tvf.TV_ERR_ALIAS),   # p_out on r_in
+    (dict(ro=(0, 8, 9)), tvf.TV_ERR_ALIAS),     # r_out on b
+    (dict(ro=(7, 11, 9)), tvf.TV_ERR_ALIAS),    # r_out on p_out
+])
+def test_step3_rejects(kw, code):
+    assert step3(**kw) == code
 
 
 def step2_h(b=0, pi=(1, 2, 3), po=(10, 11, 12), ri=(4, 5, 6), ro=(7, 8, 9), lam=0.01, m1=0.0,

@@ -121,14 +121,14 @@ def gpu_solve(tvf, b, p0, r0, lam, max_outer, n_inner, tol, variant="fused"):
     ws = torch.empty(tvf.gap_workspace_bytes(nx, ny, nz) // 8, dtype=torch.float64, device=dev)
     gd = torch.empty(3, dtype=torch.float64, device=dev)
     zws = (torch.empty_like(bt) if v == tvf.TWO_KERNEL else
-           torch.empty_like(p) if v == tvf.TB2 else None)
+           torch.empty_like(p) if v in (tvf.TB2, tvf.TB3) else None)
     done, where, gap = tvf.tv_fgp_solve(bt, p, ra, rb, lam, max_outer, n_inner, tol, ws, gd,
                                         variant=v, z_ws=zws)
     r = rb if where else ra
     return done, p.cpu().numpy(), r.cpu().numpy(), gap, gd.cpu().numpy()
 
 
-@pytest.mark.parametrize("variant", ["fused", "two_kernel", "tb2"])
+@pytest.mark.parametrize("variant", ["fused", "two_kernel", "tb2", "tb3"])
 def test_solve_stops_where_the_oracle_gap_says(tvf, variant):
     w = phantoms.workload(1)
     lam = w["lam"]

@@ -59,7 +59,7 @@ def test_volume_past_2_31_voxels_all_variants():
         ra.zero_()
         where = tvf.tv_fgp_run(bt, p, ra, rb, LAM, 1, 2, variant=v,
                                z_ws=ws if v == tvf.TWO_KERNEL else
-                               ws3 if v == tvf.TB2 else None)
+                               ws3 if v in (tvf.TB2, tvf.TB3) else None)
         r = rb if where else ra
         tvf.tv_primal(bt, p, ws, LAM)
         torch.cuda.synchronize()

@@ -19,14 +19,14 @@ pytestmark = pytest.mark.gpu
 
 TOL = 1e-5
 VARIANTS = ["fused", "lds_march", "two_kernel", "point", "reg_march", "pair", "tb2", "cube",
-            "cube_32x8x2", "cube_64x8x1", "cube_8x8x8", "cube_32x4x4"]
+            "cube_32x8x2", "cube_64x8x1", "cube_8x8x8", "cube_32x4x4", "tb3"]
 
 
 def run_workspace(tvf, v, like):
-    """The workspace a run of variant v needs: z (two-kernel) or a second p (tb2)."""
+    """The workspace a run of variant v needs: z (two-kernel) or a second p (tb2, tb3)."""
     if v == tvf.TWO_KERNEL:
         return torch.empty_like(like)
-    if v == tvf.TB2:
+    if v in (tvf.TB2, tvf.TB3):
         return torch.empty((3,) + tuple(like.shape), dtype=like.dtype, device=like.device)
     return None
 
@@ -244,6 +244,44 @@ def test_constant_input(tvf, c):
         assert np.array_equal(z, np.full_like(b, max(c, 0.0)))
 
 
+@pytest.mark.parametrize("dims", STEP2_DIMS + [(64, 8, 200), (70, 13, 9)],
+                         ids=lambda d: "x".join(map(str, d)))
+def test_step3_equals_three_oracle_steps(tvf, dims):
+    """One three-steps-per-pass launch against three oracle steps, from a state with r != p."""
+    b, p0, _ = phantoms.make_inputs(4, dims)
+    rng = np.random.default_rng(19)
+    r0 = (p0 + 0.3 * rng.standard_normal(p0.shape)).astype(np.float32)
+    m = (np.float32(0.3), np.float32(0.61), np.float32(0.7))
+    pe, re = p0, r0
+    for mk in m:
+        pe, re = oracle.step(b, pe, re, 0.003, mk)
+    dev = torch.device("cuda")
+    bt = torch.from_numpy(b).to(dev)
+    pi = torch.from_numpy(p0).to(dev)
+    ri = torch.from_numpy(r0).to(dev)
+    po = torch.full_like(pi, float("nan"))
+    ro = torch.full_like(ri, float("nan"))
+    tvf.tv_fgp_step3(bt, pi, po, ri, ro, 0.003, *(float(x) for x in m))
+    torch.cuda.synchronize()
+    got_p = po.cpu().numpy()
+    assert_bitwise((got_p, ro.cpu().numpy(), oracle.primal(b, got_p, 0.003)),
+                   (pe, re, oracle.primal(b, pe, 0.003)), "step3 %s" % (dims,))
+    assert np.array_equal(pi.cpu().numpy(), p0) and np.array_equal(ri.cpu().numpy(), r0)
+
+
+@pytest.mark.parametrize("variant", ["tb2", "tb3"])
+@pytest.mark.parametrize("no,ni", [(2, 5), (3, 4), (4, 1), (1, 7), (2, 11)],
+                         ids=lambda c: str(c))
+def test_multistep_runs_span_outer_iterations(tvf, variant, no, ni):
+    """Passes of two or three steps may cover the end of one outer iteration and
+    the start of the next (momentum restarted there); the run still equals the
+    oracle's step-by-step run bit for bit."""
+    b, p0, r0 = phantoms.make_inputs(4, (67, 21, 23))
+    exp = oracle_solve(b, p0, r0, 0.003, no, ni)
+    got = gpu_solve(tvf, b, p0, r0, 0.003, no, ni, variant)
+    assert_bitwise(got, exp, "%s %dx%d" % (variant, no, ni))
+
+
 def test_no_steps_leaves_state(tvf):
     b, p0, r0 = phantoms.make_inputs(4, (40, 10, 6))
     for no, ni in ((0, 10), (3, 0)):
@@ -295,7 +333,7 @@ def test_nan_guard_bands(tvf, variant, dims, guard):
     rb = [vol(7 + a) for a in range(3)]
     ws = vol(10) if v == tvf.TWO_KERNEL else None
     ws_store = None
-    if v == tvf.TB2:  # three consecutive volumes between guard bands
+    if v in (tvf.TB2, tvf.TB3):  # three consecutive volumes between guard bands
         ws_store = torch.full((3 * n + 2 * guard,), float("nan"), device=dev)
         ws = ws_store[guard:guard + 3 * n].view(3, nz, ny, nx)
     where = tvf.tv_fgp_run(bt, p, ra, rb, 0.003, 1, 6, variant=v, z_ws=ws)
@@ -331,7 +369,7 @@ def test_workload2_256_variants_agree(tvf):
 def test_workload3_512_full_200_steps(tvf):
     """The headline volume: all 134M voxels after the full 20 x 10 steps."""
     b, p0, r0, lam, no, ni, exp = reference(3)
-    for variant in ("fused", "pair", "tb2"):
+    for variant in ("fused", "pair", "tb2", "tb3"):
         got = gpu_solve(tvf, b, p0, r0, lam, no, ni, variant)
         assert_close(got, exp, "ellipsoids 512^3 " + variant)
         assert_bitwise(got, exp, "ellipsoids 512^3 " + variant)
@@ -389,7 +427,9 @@ def test_workload4_anisotropic_sampled(tvf):
     assert not p[0, :, :, nx - 1].any() and not p[1, :, ny - 1, :].any()
     assert not p[2, nz - 1].any()
     assert (z >= 0).all()
-    # the two-steps-per-pass run gives the same bits at every voxel
-    p2, r2, z2 = gpu_solve(tvf, b, p0, r0, lam, w["n_outer"], w["n_inner"], "tb2")
-    for name, g, e in (("p", p2, p), ("r", r2, r), ("z", z2, z)):
-        assert np.array_equal(g.view(np.uint32), e.view(np.uint32)), "tb2 vs fused " + name
+    # the two- and three-steps-per-pass runs give the same bits at every voxel
+    for variant in ("tb2", "tb3"):
+        p2, r2, z2 = gpu_solve(tvf, b, p0, r0, lam, w["n_outer"], w["n_inner"], variant)
+        for name, g, e in (("p", p2, p), ("r", r2, r), ("z", z2, z)):
+            assert np.array_equal(g.view(np.uint32), e.view(np.uint32)), variant + " vs fused " + name
+        del p2, r2, z2

@@ -25,7 +25,7 @@ SHAPES = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70)
           (126, 9, 4), (66, 10, 40), (130, 17, 33)]
 VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
             "pair_h", "pair_nostream_h", "reg_march", "point", "two_kernel", "lds_march", "primal",
-            "primal_h", "gap", "gap_pair", "tb2", "tb2_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8",
+            "primal_h", "gap", "gap_pair", "tb2", "tb2_h", "tb3", "tb3_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8",
             "cube_32x4x4"]
 FOUR_PLANE = ("tb2", "tb2_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8", "cube_32x4x4", "fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
               "pair_h", "pair_nostream_h", "point", "gap", "gap_pair")
@@ -55,6 +55,7 @@ def test_every_access_in_bounds(emul, variant):
             for end in (0, 1):
                 for grid in ((0, 7) if wide else (0,)):
                     for planes in ((8, 16, 32) if variant.startswith("tb2") else
+                                   (8, 16, 32, 96) if variant.startswith("tb3") else
                                    (8, 3) if variant not in FOUR_PLANE else (4,)):
                         args = [emul, variant, str(nx), str(ny), str(nz), str(wide), str(grid),
                                 str(end), str(planes)]

@@ -170,3 +170,53 @@ def test_two_steps_per_pass_binary16(func, tmp_path, dims, planes):
     pe, re = oracle.run_half(b, ph, rh, 0.003, 1, 2)
     assert np.array_equal(oracle.f32_to_f16_bits(pg), pe)
     assert np.array_equal(oracle.f32_to_f16_bits(rg), re)
+
+
+# (dims, 64-bit path, forced grid, slab length; 0 = as launched) for the
+# three-steps-per-pass kernel: slab ends, ragged tails, nz below a slab, one
+# voxel, tiles looped over by a short grid, each slab length the launcher picks
+CASES3 = [((65, 9, 17), 0, 0, 0), ((64, 8, 48), 1, 0, 16), ((130, 17, 33), 0, 3, 0),
+          ((1, 1, 40), 0, 0, 32), ((5, 70, 3), 0, 0, 0), ((63, 7, 15), 0, 0, 8), ((1, 1, 1), 0, 0, 0),
+          ((66, 10, 18), 1, 2, 16), ((64, 8, 200), 0, 0, 96), ((70, 13, 9), 0, 0, 8)]
+
+
+def emulate3(func, tmp_path, kernel, b, p0, r0, lam, m, wide=0, grid=0, planes=0):
+    nz, ny, nx = b.shape
+    d = str(tmp_path)
+    b.tofile(os.path.join(d, "b.bin"))
+    p0.tofile(os.path.join(d, "p.bin"))
+    r0.tofile(os.path.join(d, "r.bin"))
+    r = subprocess.run([func, kernel, str(nx), str(ny), str(nz), repr(lam), repr(float(m[0])),
+                        repr(float(m[1])), d, str(wide), str(grid), str(planes), repr(float(m[2]))],
+                       capture_output=True, text=True, timeout=300)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), r.stderr
+    pg = np.fromfile(os.path.join(d, "p_out.bin"), np.float32).reshape(p0.shape)
+    rg = np.fromfile(os.path.join(d, "r_out.bin"), np.float32).reshape(p0.shape)
+    return pg, rg
+
+
+@pytest.mark.parametrize("dims,wide,grid,planes", CASES3, ids=lambda c: str(c))
+def test_three_steps_per_pass(func, tmp_path, dims, wide, grid, planes):
+    b, p0, r0 = inputs(dims)
+    m = (np.float32(0.3), np.float32(0.61), np.float32(0.7))
+    pg, rg = emulate3(func, tmp_path, "tb3", b, p0, r0, 0.003, m, wide, grid, planes)
+    pe, re = oracle.step(b, p0, r0, 0.003, m[0])
+    pe, re = oracle.step(b, pe, re, 0.003, m[1])
+    pe, re = oracle.step(b, pe, re, 0.003, m[2])
+    assert_bits(pg, pe, "p %s" % (dims,))
+    assert_bits(rg, re, "r %s" % (dims,))
+
+
+@pytest.mark.parametrize("dims,planes", [((65, 9, 17), 0), ((64, 8, 48), 16), ((5, 70, 3), 0)],
+                         ids=lambda c: str(c))
+def test_three_steps_per_pass_binary16(func, tmp_path, dims, planes):
+    """The binary16 instantiation equals three steps of the oracle's half mode."""
+    b, p0, r0 = inputs(dims)
+    ph, rh = oracle.f32_to_f16_bits(p0), oracle.f32_to_f16_bits(r0)
+    m = [np.float32(oracle.momentum(k)) for k in (1, 2, 3)]
+    pg, rg = emulate3(func, tmp_path, "tb3_h", b, oracle.f16_bits_to_f32(ph),
+                      oracle.f16_bits_to_f32(rh), 0.003, m, 0, 0, planes)
+    pe, re = oracle.run_half(b, ph, rh, 0.003, 1, 3)
+    assert np.array_equal(oracle.f32_to_f16_bits(pg), pe)
+    assert np.array_equal(oracle.f32_to_f16_bits(rg), re)
+
