@@ -10,6 +10,8 @@
 
 #include <stdint.h>
 
+#include <tv_fgp_hwmath.hpp>
+
 #pragma clang fp contract(off)
 
 namespace tvfgp {
@@ -71,6 +73,56 @@ __device__ __forceinline__ float primal_z(float bj, float rx, float rx_lo,
   return u > 0.0f ? u : 0.0f;
 }
 
+// Correctly rounded square root of x > 1 (+inf included).  The hardware
+// estimate s is within one ulp; the residuals x - s's of its two neighbours
+// s' decide whether a neighbour is the rounded root.  This is the correction
+// the compiler wraps around v_sqrt_f32 for sqrtf, without the rescaling of
+// tiny inputs and the pass-through of zero, which inputs above 1 never need
+// (+inf comes out as +inf), so the bits are those of sqrtf.
+__device__ __forceinline__ float sqrt_above_one(float x) {
+  const float s = hw_sqrt_estimate(x);
+  const uint32_t u = __builtin_bit_cast(uint32_t, s);
+  const float sd = __builtin_bit_cast(float, u - 1u);
+  const float su = __builtin_bit_cast(float, u + 1u);
+  const float vd = __builtin_fmaf(-sd, s, x);
+  const float vu = __builtin_fmaf(-su, s, x);
+  const float t = vd <= 0.0f ? sd : s;
+  return vu > 0.0f ? su : t;
+}
+
+// 1/d from the hardware estimate and one Newton step, r + r (1 - d r): the
+// reciprocal half of the compiler's IEEE division sequence, here computed
+// once for the three quotients that share the divisor d.
+__device__ __forceinline__ float recip_refined(float d) {
+  const float r = hw_rcp_estimate(d);
+  const float e = __builtin_fmaf(-d, r, 1.0f);
+  return __builtin_fmaf(e, r, r);
+}
+
+// n / d given r = recip_refined(d): the estimate n r, two corrections by the
+// residual n - d y, then the fix-up of sign and special cases.  These are the
+// steps of the compiler's IEEE division n / d with its operand rescaling
+// left out, so the result is bit for bit the IEEE quotient wherever that
+// rescaling is the identity; it is for d in (1, 2^26) and n either zero or
+// of magnitude at least 2^-100 (quotient and divisor well inside the normal
+// range).
+__device__ __forceinline__ float div_by_refined(float n, float d, float r) {
+  float y = n * r;
+  float e = __builtin_fmaf(-d, y, n);
+  y = __builtin_fmaf(e, r, y);
+  e = __builtin_fmaf(-d, y, n);
+  y = __builtin_fmaf(e, r, y);
+  return hw_div_fixup(y, d, n);
+}
+
+// Twice the bit pattern of a (the sign shifted out) minus one, so that zero
+// wraps round to the top: the key lies below kTinyKey exactly when a is
+// nonzero with |a| < 2^-100 (whose pattern is 0x0d800000).
+__device__ __forceinline__ uint32_t tiny_key(float a) {
+  return (__builtin_bit_cast(uint32_t, a) << 1) - 1u;
+}
+constexpr uint32_t kTinyKey = 0x1affffffu;
+
 // Dual step, projection and momentum at voxel i.
 //   g_a = z(i) - z(i+e_a), 0 at the upper a-face (has_a false)
 //   q_a = r_a(i) + c * g_a,  c = 1/(12 lambda)
@@ -96,12 +148,26 @@ __device__ __forceinline__ void dual_update(float zi, float zx, float zy,
   // p' = q / 1 = q: the square root and the three divisions are skipped, and
   // a wave whose lanes all stay inside the ball skips them entirely.  NaN
   // takes the s = 1 branch, as max(1, NaN) does.
+  // Above it |q| > 1: the root comes from sqrt_above_one and, where every
+  // operand lies in div_by_refined's range (always, short of components
+  // below 2^-100 or |q| of 2^26 and more), the quotients share one refined
+  // reciprocal; elsewhere they are plain IEEE divisions.  Both give the bits
+  // of q / sqrtf(s2).
   float px = qx, py = qy, pz = qz;
   if (s2 > 0x1.000002p+0f) {
-    const float nq = __builtin_sqrtf(s2);
-    px = qx / nq;
-    py = qy / nq;
-    pz = qz / nq;
+    const float nq = sqrt_above_one(s2);
+    uint32_t key = tiny_key(qx) < tiny_key(qy) ? tiny_key(qx) : tiny_key(qy);
+    key = key < tiny_key(qz) ? key : tiny_key(qz);
+    if ((nq < 0x1p+26f) & (key >= kTinyKey)) {
+      const float rq = recip_refined(nq);
+      px = div_by_refined(qx, nq, rq);
+      py = div_by_refined(qy, nq, rq);
+      pz = div_by_refined(qz, nq, rq);
+    } else {
+      px = qx / nq;
+      py = qy / nq;
+      pz = qz / nq;
+    }
   }
   o0 = px + m * (px - p0);
   o1 = py + m * (py - p1);

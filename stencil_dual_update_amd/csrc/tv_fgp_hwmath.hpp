@@ -1,0 +1,24 @@
+// Single gfx950 instructions that the dual update builds its correctly
+// rounded square root and quotients from (tv_fgp_device.hpp).  Included as
+// <tv_fgp_hwmath.hpp> so that a host build of the kernel headers can put its
+// own stand-ins first on the include path.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+namespace tvfgp {
+
+// v_sqrt_f32: the square root, within one ulp.
+__device__ __forceinline__ float hw_sqrt_estimate(float x) { return __builtin_amdgcn_sqrtf(x); }
+
+// v_rcp_f32: the reciprocal, within one ulp.
+__device__ __forceinline__ float hw_rcp_estimate(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// v_div_fixup_f32: the last instruction of the IEEE division sequence.  It
+// returns quot with the sign of num / den, or the special value that zero,
+// infinite or NaN operands call for.
+__device__ __forceinline__ float hw_div_fixup(float quot, float den, float num) {
+  return __builtin_amdgcn_div_fixupf(quot, den, num);
+}
+
+}  // namespace tvfgp
