@@ -61,12 +61,12 @@ METRIC = "ms per FGP step at 512³ fp32; achieved HBM GB/s and % of MI355X peak"
 # from: a committed traffic record (profiles/traffic_<variant>_512.json) is
 # reported only while these sources are unchanged.
 KERNELS = {
-    "tb3": ("tb3_kernel", ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp",
+    "tb3": ("tb3_kernel", ("tv_fgp_device.hpp", "tv_fgp_hwmath.hpp", "tv_fgp_fused_kernel.hpp",
                            "tv_fgp_tb2_kernel.hpp", "tv_fgp_tb3_kernel.hpp", "tv_fgp_tb3.hip")),
-    "tb2": ("tb2_kernel", ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp",
+    "tb2": ("tb2_kernel", ("tv_fgp_device.hpp", "tv_fgp_hwmath.hpp", "tv_fgp_fused_kernel.hpp",
                            "tv_fgp_tb2_kernel.hpp", "tv_fgp_tb2.hip")),
-    "fused": ("fused_zx_kernel", ("tv_fgp_device.hpp", "tv_fgp_fused_kernel.hpp",
-                                  "tv_fgp_fused.hip")),
+    "fused": ("fused_zx_kernel", ("tv_fgp_device.hpp", "tv_fgp_hwmath.hpp",
+                                  "tv_fgp_fused_kernel.hpp", "tv_fgp_fused.hip")),
 }
 
 
