@@ -6,7 +6,9 @@ One hipcc invocation compiles the kernels and the C-ABI layer.  Flags:
   -Xclang -target-feature -Xclang -packed-fp32-ops
                            (with the leading minus) keeps the compiler from
                            emitting packed fp32 instructions
-fp32 division and square root stay correctly rounded (hipcc's default).
+fp32 division and square root stay correctly rounded (hipcc's default); the
+dual update's projection builds its own root and quotients from the same
+instruction sequences (tv_fgp_device.hpp), which give the same bits.
 """
 import glob
 import os
