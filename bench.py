@@ -176,7 +176,7 @@ def main():
         write_traffic(*args.traffic, args.variant)
         return 0
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the step would shard by z-slabs with a one-plane halo; not built). "
               "Run with --gpus 1.", file=sys.stderr)
         return 2
