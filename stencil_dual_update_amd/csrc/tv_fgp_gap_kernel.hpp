@@ -47,17 +47,41 @@ constexpr int kGapPairGrid = 1024;  // the same for the pair kernel (<= kGapGrid
 constexpr int kGapPairPlanes = 24;
 constexpr int kGapFinalBlock = 256;
 
-// Per-voxel contribution: |g|, |g| - g.p and 1/2 (z - b)^2, in fp64.
+// Square root of s for s = +0 or a finite s >= 2^-767: the compiler's
+// sqrt() sequence (the v_rsq_f64 seed, a Goldschmidt step and two residual
+// corrections, +0 passed through) without the rescaling of inputs below
+// 2^-767, which is the identity above it; a sum of squares of floats is
+// +0 or at least 2^-298.  The bits are those of sqrt().
+__device__ __forceinline__ double sqrt_sum_of_squares(double s) {
+  const double y = hw_rsq_estimate(s);
+  double g = s * y;
+  double h = y * 0.5;
+  const double r = __builtin_fma(-h, g, 0.5);
+  g = __builtin_fma(g, r, g);
+  h = __builtin_fma(h, r, h);
+  double d = __builtin_fma(-g, g, s);
+  g = __builtin_fma(d, h, g);
+  d = __builtin_fma(-g, g, s);
+  g = __builtin_fma(d, h, g);
+  return s == 0.0 ? s : g;
+}
+
+// Per-voxel contribution: |g|, |g| - g.p and (z - b)^2, in fp64 (the 1/2 of
+// the fidelity term is applied to its total, an exact scaling).  A product
+// of two floats is exact in fp64, so each multiply-add below rounds once,
+// exactly as a multiply followed by an add: the terms are those of
+// (dx dx + dy dy) + dz dz and (dx px + dy py) + dz pz.
 __device__ __forceinline__ void gap_terms(float gx, float gy, float gz, float px,
                                           float py, float pz, float z, float b,
                                           double &norm, double &gap,
                                           double &fid) {
   const double dx = (double)gx, dy = (double)gy, dz = (double)gz;
-  norm = __builtin_sqrt((dx * dx + dy * dy) + dz * dz);
-  const double dot = (dx * (double)px + dy * (double)py) + dz * (double)pz;
+  norm = sqrt_sum_of_squares(__builtin_fma(dz, dz, __builtin_fma(dx, dx, dy * dy)));
+  const double dot =
+      __builtin_fma(dz, (double)pz, __builtin_fma(dx, (double)px, dy * (double)py));
   gap = norm - dot;
   const double d = (double)z - (double)b;
-  fid = 0.5 * (d * d);
+  fid = d * d;
 }
 
 // Block-wide sum of three doubles in a fixed order; thread 0 gets the result.
@@ -405,7 +429,7 @@ __global__ __launch_bounds__(kGapFinalBlock) void gap_final_kernel(
   if (threadIdx.x == 0) {
     out[0] = lam * a;
     out[1] = c;
-    out[2] = d;
+    out[2] = 0.5 * d;
   }
 }
 

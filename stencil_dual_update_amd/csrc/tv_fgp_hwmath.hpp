@@ -1,5 +1,6 @@
 // Single gfx950 instructions that the dual update builds its correctly
-// rounded square root and quotients from (tv_fgp_device.hpp).  Included as
+// rounded square root and quotients from (tv_fgp_device.hpp), and the
+// duality gap its double square root (tv_fgp_gap_kernel.hpp).  Included as
 // <tv_fgp_hwmath.hpp> so that a host build of the kernel headers can put its
 // own stand-ins first on the include path.
 #pragma once
@@ -13,6 +14,10 @@ __device__ __forceinline__ float hw_sqrt_estimate(float x) { return __builtin_am
 
 // v_rcp_f32: the reciprocal, within one ulp.
 __device__ __forceinline__ float hw_rcp_estimate(float x) { return __builtin_amdgcn_rcpf(x); }
+
+// v_rsq_f64: the reciprocal square root of a double, to about single
+// precision (the seed of the double square root's refinement).
+__device__ __forceinline__ double hw_rsq_estimate(double x) { return __builtin_amdgcn_rsq(x); }
 
 // v_div_fixup_f32: the last instruction of the IEEE division sequence.  It
 // returns quot with the sign of num / den, or the special value that zero,

@@ -31,6 +31,8 @@ inline float hw_rcp_estimate(float x) {
   return other_side(rn, (double)rn * (double)x < 1.0);
 }
 
+inline double hw_rsq_estimate(double x) { return 1.0 / sqrt(x); }
+
 inline float hw_div_fixup(float quot, float den, float num) {
   const bool neg = signbit(den) != signbit(num);
   if (num == 0.0f) return neg ? -0.0f : 0.0f;

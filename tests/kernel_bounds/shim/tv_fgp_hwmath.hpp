@@ -14,6 +14,8 @@ inline float hw_sqrt_estimate(float x) { return sqrtf(x); }
 
 inline float hw_rcp_estimate(float x) { return 1.0f / x; }
 
+inline double hw_rsq_estimate(double x) { return 1.0 / sqrt(x); }
+
 // The cases the dual update reaches: a finite divisor above 1 and a finite
 // numerator; the quotient takes the sign of num / den, a zero numerator gives
 // a zero of that sign.

@@ -2,7 +2,9 @@
 (tv_fgp_device.hpp: sqrt_above_one, recip_refined, div_by_refined) on the
 GPU, against the host's IEEE float32 sqrt and division (numpy), which the
 projection p' = q / max(1, |q|) of the page "TV solver: the FGP step on the
-GPU" (section "What one step does") is defined with.
+GPU" (section "What one step does") is defined with; and the duality gap's
+double square root (tv_fgp_gap_kernel.hpp: sqrt_sum_of_squares) against the
+compiler's and numpy's.
 
 The kernels come from tests/device_math/libdevmath.so (built by
 __graft_entry__.build()).  Checked: every float above 1 for the square root;
@@ -39,6 +41,9 @@ def dm():
         getattr(lib, name).restype = ctypes.c_int
     lib.devmath_div.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p]
     lib.devmath_div.restype = ctypes.c_int
+    lib.devmath_sqrt64.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.devmath_sqrt64.restype = ctypes.c_int
     return lib
 
 
@@ -133,3 +138,41 @@ def test_quotients_match_ieee_division(dm):
     miss = np.nonzero(got != want)[0]
     assert len(miss) == 0, (len(miss), [(float(num[i]), float(den[i]), hex(int(got[i])),
                                          hex(int(want[i]))) for i in miss[:6]])
+
+
+def sums_of_squares(seed=11, n=1 << 22):
+    """Sums (x*x + y*y) + z*z of float triples, in fp64, as the gap forms
+    them: random magnitudes over the whole float range, zeros, single
+    nonzero components (exact squares), the smallest subnormal."""
+    rng = np.random.default_rng(seed)
+    def floats(k):
+        f = np.ldexp(1.0 + rng.integers(0, 1 << 23, k) / 2.0 ** 23,
+                     rng.integers(-149, 128, k)).astype(np.float32)
+        return np.where(rng.random(k) < 0.1, np.float32(0), f).astype(np.float64)
+    x, y, z = floats(n), floats(n), floats(n)
+    with np.errstate(over="ignore"):
+        s = (x * x + y * y) + z * z
+    s = s[np.isfinite(s)]
+    tiny = np.float64(np.float32(2.0 ** -149)) ** 2
+    extra = np.array([0.0, tiny, 2 * tiny, 1.0, 2.0, 4.0, 0.25, 3.0, 1e-30, 1e30, 1e77], np.float64)
+    return np.concatenate([s, extra, x * x])
+
+
+def test_gap_sqrt_matches_ieee(dm):
+    """sqrt_sum_of_squares(s) == sqrt(s) bit for bit, against the compiler's
+    double square root and numpy's IEEE one, over sums of squares of
+    floats (+0 or at least 2^-298)."""
+    import torch
+    s = sums_of_squares()
+    assert np.all((s == 0) | ((s >= 2.0 ** -298) & np.isfinite(s)))
+    ts = torch.from_numpy(s).cuda()
+    out = torch.empty_like(ts)
+    ref = torch.empty_like(ts)
+    assert ts.numel() == out.numel() == ref.numel()
+    assert dm.devmath_sqrt64(ts.data_ptr(), ts.numel(), out.data_ptr(), ref.data_ptr()) == 0
+    got = out.cpu().numpy().view(np.uint64)
+    comp = ref.cpu().numpy().view(np.uint64)
+    want = np.sqrt(s).view(np.uint64)
+    assert np.array_equal(got, comp), int(np.count_nonzero(got != comp))
+    miss = np.nonzero(got != want)[0]
+    assert len(miss) == 0, (len(miss), [float(s[i]) for i in miss[:6]])
