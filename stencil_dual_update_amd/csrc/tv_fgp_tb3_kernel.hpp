@@ -24,8 +24,9 @@
 //   R1 = [-1, 65] x [-1,  9]  primal z1 of r1              67 x 11
 //   E2 = [-1, 64] x [-1,  8]  step two  -> p2, r2          66 x 10
 //   R2 = [ 0, 64] x [ 0,  8]  primal z2 of r2              65 x  9
-// Thread t owns tile point (t % 64, t / 64); threads 0..384 also own one of
-// the 385 points of R0 outside the tile.
+// Thread t owns tile point (t % 64, t / 64); threads 0..383 (waves 0-5) also
+// own one of the 384 points of R0 outside the tile that a step reads (its
+// corner (66, 10) is never read), so waves 6 and 7 carry no halo point.
 //
 // Iteration k of the z march (k from z0 - 7 to z1 - 1 for the slab [z0, z1)):
 //   phase 1: z2 at plane k+1 on R2, z1 at plane k+3 on R1, z0 at plane k+5
@@ -58,18 +59,18 @@ constexpr int kT3E1X = kTbTileX + 4, kT3E1Y = kTbTileY + 4;  // 68 x 12
 constexpr int kT3R1X = kTbTileX + 3, kT3R1Y = kTbTileY + 3;  // 67 x 11
 constexpr int kT3E2X = kTbTileX + 2, kT3E2Y = kTbTileY + 2;  // 66 x 10
 constexpr int kT3R2X = kTbTileX + 1, kT3R2Y = kTbTileY + 1;  // 65 x  9
-constexpr int kT3Halo = kT3R0X * kT3R0Y - kTbTileX * kTbTileY;  // 385
+constexpr int kT3Halo = kT3R0X * kT3R0Y - kTbTileX * kTbTileY - 1;  // 384
 
 // Tile coordinates of the h-th R0 point outside the tile: the rows y = -2,
-// -1, 8, 9, 10 (x = -2..66), then the columns x = -2, -1, 64, 65, 66
-// (y = 0..7).
+// -1, 8, 9, 10 (x = -2..66, the last row without x = 66), then the columns
+// x = -2, -1, 64, 65, 66 (y = 0..7).
 __device__ __forceinline__ void tb3_halo_point(int h, int &x, int &y) {
-  if (h < 5 * kT3R0X) {
+  if (h < 5 * kT3R0X - 1) {
     const int row = h / kT3R0X;
     y = row < 2 ? row - 2 : kTbTileY + row - 2;
     x = h % kT3R0X - 2;
   } else {
-    const int c = h - 5 * kT3R0X;
+    const int c = h - (5 * kT3R0X - 1);
     const int col = c / kTbTileY;
     y = c % kTbTileY;
     x = col < 2 ? col - 2 : kTbTileX + col - 2;
