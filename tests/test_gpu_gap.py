@@ -1,9 +1,10 @@
 """GPU duality gap and the convergence-checked solve, against the CPU oracle.
 
 The gap kernel computes z and g = Dz in fp32 exactly as the oracle does (bit
-for bit), the per-voxel terms in fp64 with the same operation order, and sums
-them in a different but fixed order; so the results agree to fp64 summation
-error (relative 1e-10 is required) and repeated GPU calls agree bit for bit.
+for bit), the per-voxel terms in fp64 with the same roundings (multiply-adds
+of exact products, the fidelity's 1/2 applied to its total), and sums them in
+a different but fixed order; so the results agree to fp64 summation error
+(relative 1e-10 is required) and repeated GPU calls agree bit for bit.
 """
 import numpy as np
 import pytest
