@@ -119,6 +119,10 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
   const bool has_halo = tid < kT3Halo;
   int hlx = 0, hly = 0;
   if (has_halo) tb3_halo_point(tid, hlx, hly);
+  // The halo waves (0-5) carry more work between barriers than waves 6 and
+  // 7, so they issue first (1% at 512^3).  The branch is on a scalar, so the
+  // priority instruction runs in those waves only.
+  if (hw_wave_uniform(tid) < kT3Halo) hw_raise_priority();
   const Off sy4 = g.sy4, sz4 = g.sz4;
 
   for (I t = (I)blockIdx.x; t < g.ntiles; t += (I)gridDim.x) {

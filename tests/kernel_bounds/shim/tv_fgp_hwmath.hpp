@@ -16,6 +16,10 @@ inline float hw_rcp_estimate(float x) { return 1.0f / x; }
 
 inline double hw_rsq_estimate(double x) { return 1.0 / sqrt(x); }
 
+// One thread stands for its wave, and there is no issue priority.
+inline int hw_wave_uniform(int v) { return v; }
+inline void hw_raise_priority() {}
+
 // The cases the dual update reaches: a finite divisor above 1 and a finite
 // numerator; the quotient takes the sign of num / den, a zero numerator gives
 // a zero of that sign.
