@@ -77,12 +77,32 @@ __device__ __forceinline__ void tb3_halo_point(int h, int &x, int &y) {
   }
 }
 
+// Six floats carried from one plane step to the next as three 64-bit pairs
+// (p0, p1), (p2, r0), (r1, r2): handing a set on is then three 64-bit
+// register moves instead of six 32-bit ones.
+struct Tb3Six {
+  uint64_t a, b, c;
+};
+
+__device__ __forceinline__ uint64_t tb3_pair(float lo, float hi) {
+  return (uint64_t)__builtin_bit_cast(uint32_t, lo) |
+         ((uint64_t)__builtin_bit_cast(uint32_t, hi) << 32);
+}
+__device__ __forceinline__ float tb3_lo(uint64_t v) { return __builtin_bit_cast(float, (uint32_t)v); }
+__device__ __forceinline__ float tb3_hi(uint64_t v) {
+  return __builtin_bit_cast(float, (uint32_t)(v >> 32));
+}
+__device__ __forceinline__ Tb3Six tb3_six(float p0, float p1, float p2, float r0, float r1,
+                                         float r2) {
+  return Tb3Six{tb3_pair(p0, p1), tb3_pair(p2, r0), tb3_pair(r1, r2)};
+}
+
 // Region membership of a point and the state it carries beyond TbPoint.
 struct Tb3Extra {
   bool e1, r1, e2, r2;
-  float b2, b1;                        // b of planes k+2 and k+1
-  float p1a0, p1a1, p1a2, r1a0, r1a1, r1a2;  // step one's p1, r1 of plane k+2
-  float p1b0, p1b1, p1b2, r1b0, r1b1, r1b2;  // ... of plane k+3
+  float b2, b1;   // b of planes k+2 and k+1
+  Tb3Six pr1a;    // step one's p1, r1 of plane k+2
+  Tb3Six pr1b;    // ... of plane k+3
 };
 
 __device__ __forceinline__ void tb3_init_extra(Tb3Extra &e, int lx, int ly) {
@@ -91,8 +111,7 @@ __device__ __forceinline__ void tb3_init_extra(Tb3Extra &e, int lx, int ly) {
   e.e2 = lx >= -1 && lx <= kTbTileX && ly >= -1 && ly <= kTbTileY;
   e.r2 = lx >= 0 && lx <= kTbTileX && ly >= 0 && ly <= kTbTileY;
   e.b2 = e.b1 = 0.0f;
-  e.p1a0 = e.p1a1 = e.p1a2 = e.r1a0 = e.r1a1 = e.r1a2 = 0.0f;
-  e.p1b0 = e.p1b1 = e.p1b2 = e.r1b0 = e.r1b1 = e.r1b2 = 0.0f;
+  e.pr1a = e.pr1b = Tb3Six{0, 0, 0};
 }
 
 // Four waves per SIMD (two workgroups per CU): the carried state of three
@@ -139,8 +158,7 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
     tb3_init_extra(ox, own.lx, own.ly);
     tb3_init_extra(hx, hal.lx, hal.ly);
     // own p2, r2 of planes k and k+1 (step two at the thread's tile point)
-    float pa0 = 0.0f, pa1 = 0.0f, pa2 = 0.0f, ra0 = 0.0f, ra1 = 0.0f, ra2 = 0.0f;
-    float pb0 = 0.0f, pb1 = 0.0f, pb2 = 0.0f, rb0 = 0.0f, rb1 = 0.0f, rb2 = 0.0f;
+    Tb3Six pra{0, 0, 0}, prb{0, 0, 0};
 
     const I kstart = z0 - 7;
     // planes whose inputs the slab reads: [z0 - 2, z1 + 2] (and r_z of z0 - 3)
@@ -237,8 +255,9 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
         const float zi = z2r[s][y][x], zx = z2r[s][y][x + 1], zy = z2r[s][y + 1][x];
         const float zz = z2r[sn][y][x];
         float o0, o1, o2;
-        dual_update(zi, zx, zy, zz, own.has_x, own.has_y, k + 1 < g.nz, ra0, ra1, ra2,
-                    pa0, pa1, pa2, c, m3, o0, o1, o2);
+        float pa0 = tb3_lo(pra.a), pa1 = tb3_hi(pra.a), pa2 = tb3_lo(pra.b);
+        dual_update(zi, zx, zy, zz, own.has_x, own.has_y, k + 1 < g.nz, tb3_hi(pra.b),
+                    tb3_lo(pra.c), tb3_hi(pra.c), pa0, pa1, pa2, c, m3, o0, o1, o2);
         const Off j = own.o + (Off)k * sz4;
         sts_stream(po0, j, pa0);
         sts_stream(po1, j, pa1);
@@ -247,24 +266,17 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
         sts_stream(ro1, j, o1);
         sts_stream(ro2, j, o2);
       }
-      pa0 = pb0;
-      pa1 = pb1;
-      pa2 = pb2;
-      ra0 = rb0;
-      ra1 = rb1;
-      ra2 = rb2;
+      pra = prb;
       // step two at an E2 point from its step-one p1, r1 of plane k+2
-      auto phase_d2 = [&](TbPoint<Off> &pt, Tb3Extra &e, float &p0o, float &p1o, float &p2o,
-                          float &r0o, float &r1o, float &r2o) {
+      auto phase_d2 = [&](TbPoint<Off> &pt, Tb3Extra &e, Tb3Six &out) {
         const int x = pt.lx + 1, y = pt.ly + 1;
         const int s = (int)(kd2 & 1), sn = (int)((kd2 + 1) & 1);
         const float zi = z1r[s][y][x], zx = z1r[s][y][x + 1], zy = z1r[s][y + 1][x];
         const float zz = z1r[sn][y][x];
-        p0o = e.p1a0;
-        p1o = e.p1a1;
-        p2o = e.p1a2;
-        dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd2 + 1 < g.nz, e.r1a0, e.r1a1,
-                    e.r1a2, p0o, p1o, p2o, c, m2, r0o, r1o, r2o);
+        float p0o = tb3_lo(e.pr1a.a), p1o = tb3_hi(e.pr1a.a), p2o = tb3_lo(e.pr1a.b);
+        float r0o, r1o, r2o;
+        dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd2 + 1 < g.nz, tb3_hi(e.pr1a.b),
+                    tb3_lo(e.pr1a.c), tb3_hi(e.pr1a.c), p0o, p1o, p2o, c, m2, r0o, r1o, r2o);
         p0o = as_stored<S>(p0o);
         p1o = as_stored<S>(p1o);
         p2o = as_stored<S>(p2o);
@@ -274,24 +286,17 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
         r2x[y][x] = r0o;
         r2y[y][x] = r1o;
         r2z[s][y][x] = r2o;
+        out = tb3_six(p0o, p1o, p2o, r0o, r1o, r2o);
       };
       if (do_d2) {
-        if (own.ok) phase_d2(own, ox, pb0, pb1, pb2, rb0, rb1, rb2);
+        if (own.ok) phase_d2(own, ox, prb);
         if (hal.ok && hx.e2) {
-          float q0, q1, q2, s0, s1, s2;
-          phase_d2(hal, hx, q0, q1, q2, s0, s1, s2);
+          Tb3Six unused;
+          phase_d2(hal, hx, unused);
         }
       }
-      auto shift1 = [](Tb3Extra &e) {
-        e.p1a0 = e.p1b0;
-        e.p1a1 = e.p1b1;
-        e.p1a2 = e.p1b2;
-        e.r1a0 = e.r1b0;
-        e.r1a1 = e.r1b1;
-        e.r1a2 = e.r1b2;
-      };
-      shift1(ox);
-      shift1(hx);
+      ox.pr1a = ox.pr1b;
+      hx.pr1a = hx.pr1b;
       // step one at an E1 point from the input r and p of plane k+4
       auto phase_d1 = [&](TbPoint<Off> &pt, Tb3Extra &e) {
         const int x = pt.lx + 2, y = pt.ly + 2;
@@ -301,15 +306,14 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
         float r0o, r1o, r2o;
         dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd1 + 1 < g.nz, pt.q0, pt.q1, pt.q2,
                     pt.pp0, pt.pp1, pt.pp2, c, m1, r0o, r1o, r2o);
-        e.p1b0 = as_stored<S>(pt.pp0);
-        e.p1b1 = as_stored<S>(pt.pp1);
-        e.p1b2 = as_stored<S>(pt.pp2);
-        e.r1b0 = as_stored<S>(r0o);
-        e.r1b1 = as_stored<S>(r1o);
-        e.r1b2 = as_stored<S>(r2o);
-        r1x[y][x] = e.r1b0;
-        r1y[y][x] = e.r1b1;
-        r1z[s][y][x] = e.r1b2;
+        r0o = as_stored<S>(r0o);
+        r1o = as_stored<S>(r1o);
+        r2o = as_stored<S>(r2o);
+        e.pr1b = tb3_six(as_stored<S>(pt.pp0), as_stored<S>(pt.pp1), as_stored<S>(pt.pp2), r0o,
+                         r1o, r2o);
+        r1x[y][x] = r0o;
+        r1y[y][x] = r1o;
+        r1z[s][y][x] = r2o;
       };
       if (do_d1) {
         if (own.ok) phase_d1(own, ox);
