@@ -8,10 +8,10 @@
 // by two voxels in x and y, step two on the tile grown by one, step three on
 // the tile, keeping the intermediate p and r on chip: b, p and r are read
 // once and p, r written once per three steps.  On MI355X at 512^3 a launch
-// takes 2.00 ms, 0.67 ms per step (two steps per pass: 0.76; one: 1.29); its
-// L2 traffic is 1.31-1.36 x the compulsory bytes, moved at 4.6 TB/s, and it
-// issues VALU instructions three quarters of the time, so at two workgroups
-// per CU the pass is bound by its arithmetic and latency, not by memory.
+// takes 1.94 ms, 0.65 ms per step (two steps per pass: 0.76; one: 1.30); its
+// L2 traffic is 1.31-1.36 x the compulsory bytes, moved at 4.7 TB/s, and it
+// issues VALU instructions 70% of the time, so at two workgroups per CU the
+// pass is bound by instruction issue and latency, not by memory.
 //
 // Every value is computed by the same device functions in the same order as
 // the one-step kernels (primal_z, dual_update), so three launches of those and
@@ -115,7 +115,7 @@ __device__ __forceinline__ void tb3_init_extra(Tb3Extra &e, int lx, int ly) {
 }
 
 // Four waves per SIMD (two workgroups per CU): the carried state of three
-// levels takes 119 VGPRs; capping at six waves spilled 53 and ran 2.8x slower.
+// levels takes 125 VGPRs; capping at six waves spilled 53 and ran 2.8x slower.
 template <typename I, typename Off, typename S>
 __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
     const float *__restrict__ b, const S *__restrict__ pi0,
