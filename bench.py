@@ -7,7 +7,10 @@ steps, lambda = 0.002, run by tv_fgp_run with the three-steps-per-pass kernel
 three one-step launches; 200 steps = 66 launches of three and one of two).
 The timed region runs exactly --steps steps (in outer iterations of 10,
 momentum restarted at each) on one stream, bracketed by device
-synchronisation; inputs are resident in HBM before it starts.
+synchronisation; inputs are resident in HBM before it starts.  It is run three
+times and `value` is the median (the page reports medians of repeated solves);
+`config.timed` lists the launches one timed region makes and whether p ends in
+the workspace and is copied back.
 
 Besides the headline ms/step it reports:
   roofline      algorithmic bytes per launch (52 B per voxel: read b, r (3),
@@ -30,10 +33,17 @@ Besides the headline ms/step it reports:
                 median and spread) and T0, the same solve with zero dual steps
                 per outer iteration, with (T - T0) / steps
   copy          bandwidth of a plain device copy of 2 x 1 GiB on the same box
-  cpu_baseline  the CPU oracle (fp32, OpenMP) timed on the host cores on a
-                bounded sample: the first 10 outer iterations (100 steps) of
-                the same workload at full size (with --storage half: the first
-                outer iteration, 10 steps, of the oracle's half mode)
+  ceiling       tv_fgp_stream_probe: the 7-read / 6-write traffic of one step
+                over the same volume size as a linear stream with
+                non-temporal stores, the bandwidth a step kernel's bytes can
+                reach here; one_step_kernel.pct_of_ceiling and
+                roofline.pct_of_ceiling set the kernels against it
+  cpu_baseline  the CPU oracle (fp32, OpenMP over z planes) timed on the host
+                cores on a bounded sample: the first 10 outer iterations (100
+                steps) of the same workload at full size (with --storage half:
+                the first outer iteration, 10 steps, of the oracle's half
+                mode) on up to 16 threads, plus 5 steps (half: 2) on one
+                thread; with the thread count, nproc and the CPU model
 
 --storage half runs the step with p and r stored as binary16 (fp32
 arithmetic; 28 B per voxel: read b, r (3), p (3) at 4 + 6 + 6 B, write p (3),
@@ -74,12 +84,41 @@ def traffic_file(variant):
     return os.path.join(ROOT, "profiles", "traffic_%s_512.json" % variant)
 
 
+def strip_comments(text):
+    """C/C++ source without its comments and with whitespace runs collapsed,
+    so that an edit of comments or layout leaves the digest unchanged.
+    String and character literals are kept as they are."""
+    out = []
+    i, n = 0, len(text)
+    while i < n:
+        ch = text[i]
+        if ch in "\"'":
+            j = i + 1
+            while j < n and text[j] != ch:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            j = text.find("\n", i)
+            i = n if j < 0 else j
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+            out.append(" ")
+        else:
+            out.append(ch)
+            i += 1
+    return " ".join("".join(out).split())
+
+
 def kernel_source_digest(variant):
+    """Digest of the device code a variant's kernel is built from (comments
+    and layout excluded)."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "stencil_dual_update_amd", "csrc")
     for name in KERNELS[variant][1]:
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            h.update(name.encode() + b"\0" + strip_comments(f.read()).encode())
     return h.hexdigest()
 
 
@@ -144,6 +183,17 @@ def write_traffic(fetch_csv, write_csv, variant):
     print(json.dumps(rec))
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,8 +203,8 @@ def parse():
     ap.add_argument("--dims", type=int, nargs=3, metavar=("NX", "NY", "NZ"),
                     help="run the workload's recipe at other dimensions")
     ap.add_argument("--variant", default=None, choices=sorted(BYTES_PER_VOXEL),
-                    help="kernel variant (default: tb2, two steps per pass; fused with "
-                         "--storage half)")
+                    help="kernel variant (default: tb3, three steps per pass; with "
+                         "--storage half: tb2, two steps per pass)")
     ap.add_argument("--no-cpu-baseline", action="store_true",
                     help="skip the CPU oracle leg")
     ap.add_argument("--storage", default="f32", choices=["f32", "half"],
@@ -231,6 +281,29 @@ def main():
             tvf.tv_fgp_step(b, p, r_cur, r_nxt, lam, m, variant=variant, z_ws=ws,
                             stream=stream)
 
+    def passes_of(k):
+        """Launches tv_fgp_run makes for k steps in outer iterations of n_inner
+        (passes of three and two steps, single steps) and whether p ends in
+        the workspace and is copied back."""
+        full, rest = divmod(k, n_inner)
+        counts = {3: 0, 2: 0, 1: 0}
+        copies = 0
+        for n_outer, ni in ((full, n_inner), (1 if rest else 0, rest)):
+            left = n_outer * ni
+            flips = 0
+            while left > 0:
+                if spl >= 3 and (left >= 5 or left == 3):
+                    todo = 3
+                elif spl >= 2:
+                    todo = 2 if left >= 2 else 1
+                else:
+                    todo = 1
+                counts[todo] += 1
+                flips += todo > 1
+                left -= todo
+            copies += flips % 2
+        return counts, copies
+
     def run_steps(k, r_cur, r_nxt):
         """k steps in outer iterations of n_inner; returns (r_cur, r_nxt) after."""
         full, rest = divmod(k, n_inner)
@@ -297,13 +370,15 @@ def main():
         p = p_cur
         launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
 
-    ms_per_step = region_ms / args.steps
+    # the reported figure is the median of the three timed regions (the page
+    # reports medians of repeated solves)
     runs = sorted([region_ms] + repeat_ms)
+    ms_per_step = runs[1] / args.steps
     repeats = {"ms_per_step": [round(v / args.steps, 5) for v in [region_ms] + repeat_ms],
-               "median_ms_per_step": round(runs[1] / args.steps, 5),
+               "median_ms_per_step": round(ms_per_step, 5),
                "spread_pct": round(100.0 * (runs[-1] - runs[0]) / runs[1], 2),
                "t0_ms": round(t0_ms, 4),
-               "t_minus_t0_ms_per_step": round((region_ms - t0_ms) / args.steps, 5)}
+               "t_minus_t0_ms_per_step": round((runs[1] - t0_ms) / args.steps, 5)}
     step_bytes = (BYTES_PER_VOXEL_HALF if half else BYTES_PER_VOXEL[args.variant]) * nvox
     launch_avg_ms = float(np.mean(launch_ms))
     achieved = step_bytes / (launch_avg_ms * 1e-3) / 1e9
@@ -384,30 +459,95 @@ def main():
                 "gbps": round(2 * src.numel() * 4 / (copy_ms * 1e-3) / 1e9, 1)}
         del src, dst
 
+    # the same 7-read / 6-write traffic as one step, as a plain linear stream
+    # with non-temporal stores: what the part achieves for a step's bytes
+    ceiling = None
+    pct_ceiling = None
+    if not args.no_copy and not half:
+        vols = [torch.empty(nvox, dtype=torch.float32, device=dev).fill_(0.5)
+                for _ in range(13)]
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                tvf.tv_fgp_stream_probe(vols[:7], vols[7:], stream=stream)
+            c0 = torch.cuda.Event(enable_timing=True)
+            c1 = torch.cuda.Event(enable_timing=True)
+            c0.record(stream)
+            reps = 20
+            for _ in range(reps):
+                tvf.tv_fgp_stream_probe(vols[:7], vols[7:], stream=stream)
+            c1.record(stream)
+            torch.cuda.synchronize()
+        ceil_ms = c0.elapsed_time(c1) / reps
+        ceil_gbs = 52 * nvox / (ceil_ms * 1e-3) / 1e9
+        ceiling = {"kernel": "stream13_kernel", "bytes": 52 * nvox, "ms": round(ceil_ms, 5),
+                   "gbps": round(ceil_gbs, 1), "frac_of_hbm_peak": round(ceil_gbs / HBM_PEAK_GBS, 4)}
+        if one_step is not None:
+            one_step["pct_of_ceiling"] = round(100.0 * ceil_ms / one_step["ms_per_step"], 1)
+        if args.variant in ("fused", "tb2", "tb3"):
+            # compulsory bytes of a launch (52 B per voxel) at the ceiling's rate
+            # against the launch's time
+            pct_ceiling = round(100.0 * ceil_ms / launch_avg_ms, 1)
+        del vols
+
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
-        threads = min(16, os.cpu_count() or 1)
-        oracle.set_threads(threads)
+        nproc = os.cpu_count() or 1
+        try:
+            usable = len(os.sched_getaffinity(0))
+        except AttributeError:
+            usable = nproc
+        # the GPU machine's CPU share is 16 threads whatever the machine shows
+        threads = min(16, usable)
         p0 = p0_host
-        cpu_outer = 1 if half else 10  # the half mode converts p, r every step: slower
         if half:
             p0 = oracle.f32_to_f16_bits(p0)
-        t1 = time.perf_counter()
-        if half:
-            oracle.run_half(b_host, p0, p0, lam, cpu_outer, n_inner)
-        else:
-            oracle.run(b_host, p0, p0, lam, cpu_outer, n_inner)
-        cpu_s = time.perf_counter() - t1
+
+        def oracle_sample(n_outer, ni):
+            t1 = time.perf_counter()
+            if half:
+                oracle.run_half(b_host, p0, p0, lam, n_outer, ni)
+            else:
+                oracle.run(b_host, p0, p0, lam, n_outer, ni)
+            return time.perf_counter() - t1
+
+        cpu_outer = 1 if half else 10  # the half mode converts p, r every step: slower
+        oracle.set_threads(threads)
+        cpu_s = oracle_sample(cpu_outer, n_inner)
+        used = oracle.get_threads()
         cpu_steps = cpu_outer * n_inner
+        one_steps = 2 if half else 5
+        oracle.set_threads(1)
+        one_s = oracle_sample(1, one_steps)
+        oracle.set_threads(threads)
         cpu = {"value": round(cpu_s * 1e3 / cpu_steps, 3), "unit": "ms/step",
-               "cores": oracle.get_threads(), "kind": "oracle",
+               "cores": used, "kind": "oracle",
                "sample": "first %d outer iterations (%d steps) of the same workload at "
-                         "full size, fp32 exact-order oracle%s, %.1f s" % (
+                         "full size, fp32 exact-order oracle%s, OpenMP over z planes, "
+                         "%d threads, %.1f s" % (
                              cpu_outer, cpu_steps, " (binary16 dual)" if half else "",
-                             cpu_s)}
+                             used, cpu_s),
+               "threads": used, "nproc": nproc, "usable_cpus": usable,
+               "cpu_model": cpu_model(),
+               "one_thread": {"value": round(one_s * 1e3 / one_steps, 3), "unit": "ms/step",
+                              "sample": "first %d steps of the same workload at full size, "
+                                        "1 thread, %.1f s" % (one_steps, one_s)}}
 
     traffic = None if (args.dims or half) else measured_traffic(args.variant, args.workload)
+    base = phantoms.BASE_NAMES[args.workload]
+    if args.dims:
+        base = "%s recipe at %dx%dx%d" % (base, nx, ny, nz)
+    counts, copies = passes_of(args.steps)
+    full, rest = divmod(args.steps, n_inner)
+    workload_label = "%s, lambda %g: %d steps timed (%s), median of 3 timed runs" % (
+        base, lam, args.steps,
+        " + ".join(x for x in ("%d outer x %d inner" % (full, n_inner) if full else "",
+                               "1 outer x %d inner" % rest if rest else "") if x))
+    timed = {"steps": args.steps,
+             "launches": {"three_step": counts[3], "two_step": counts[2],
+                          "one_step": counts[1]},
+             "p_copy_back": copies > 0,
+             "runs": 3}
     out = {
         "metric": METRIC if not half else METRIC.replace("fp32", "fp32 with binary16 p, r"),
         "value": round(ms_per_step, 5),
@@ -421,8 +561,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": phantoms.NAMES[args.workload] if not args.dims else
-                   "%s recipe at %dx%dx%d" % (phantoms.NAMES[args.workload], nx, ny, nz),
+        "config": {"workload": workload_label, "timed": timed,
                    "dims": [nx, ny, nz], "lambda": lam, "steps_per_outer": n_inner,
                    "variant": args.variant, "dual_storage": "binary16" if half else "f32",
                    "parallelism": "single GPU"},
@@ -436,7 +575,8 @@ def main():
                      "steps_per_launch": spl,
                      "launch_ms_avg": round(launch_avg_ms, 5),
                      "launch_ms_min": round(float(np.min(launch_ms)), 5),
-                     "launch_ms_max": round(float(np.max(launch_ms)), 5)},
+                     "launch_ms_max": round(float(np.max(launch_ms)), 5),
+                     "pct_of_ceiling": pct_ceiling},
         "one_step_kernel": one_step,
         "repeats": repeats,
         # a pass that does one step moves 52 B per voxel per step: its time at
@@ -449,6 +589,7 @@ def main():
         "gap_kernel": gap,
         "copy": copy,
         "pct_of_copy": (round(100.0 * region_gbs / copy["gbps"], 1) if copy else None),
+        "ceiling": ceiling,
         "cpu_baseline": cpu,
         "wall_ms_timed_region": round(wall_ms, 2),
         "input_gen_s": round(gen_s, 2),

@@ -324,6 +324,25 @@ size_t tv_fgp_workspace_bytes(int variant, int64_t nx, int64_t ny, int64_t nz);
  */
 float tv_fgp_momentum(int k);
 
+/*
+ * Measurement helper, not a step: moves the traffic of one fused step as a
+ * plain linear stream, so that a step kernel's time can be set against what
+ * the part achieves for the same bytes.  The page "TV solver: the FGP step on
+ * the GPU" (section "Profiler counters" and its closing paragraph) prices a
+ * fused step at 13 volumes, 7 read (b, p, r) and 6 written (p, r).  This call
+ * writes dst[k][i] = src[k][i] + src[6][i] for k = 0..5 and i < n, reading
+ * every src volume once (16-byte loads) and writing every dst volume once
+ * (non-temporal 16-byte stores).
+ *   src  [in]  7 device volumes of n floats, 16-byte aligned
+ *   dst  [out] 6 device volumes of n floats, 16-byte aligned
+ *   n    elements per volume, >= 1
+ * No dst may overlap any other volume of the call.  Errors: TV_ERR_NULL,
+ * TV_ERR_DIMS (n < 1 or n*4 overflows), TV_ERR_ALIGN, TV_ERR_ALIAS,
+ * TV_ERR_LAUNCH.  Enqueued on `stream`, no host synchronisation.
+ */
+int tv_fgp_stream_probe(const float *const src[7], float *const dst[6], int64_t n,
+                        void *stream);
+
 /* Static, NUL-terminated description of a status code. */
 const char *tv_fgp_status_string(int status);
 

@@ -46,6 +46,14 @@ WORKLOADS = {
             kind="uniform_ellipsoids", n_obj=16, noise=0.0, init="ball"),
 }
 
+BASE_NAMES = {
+    0: "blobs 32^3",
+    1: "blobs 128^3",
+    2: "ellipsoids 256^3",
+    3: "ellipsoids 512^3",
+    4: "uniform+ellipsoids 1000x777x301",
+}
+
 NAMES = {
     0: "blobs 32^3, 10 steps",
     1: "blobs 128^3, 20x10 steps",

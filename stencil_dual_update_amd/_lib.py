@@ -39,8 +39,8 @@ VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
 EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_fgp_step2", "tv_fgp_step3",
            "tv_primal",
            "tv_fgp_step_h", "tv_fgp_run_h", "tv_fgp_step2_h", "tv_fgp_run2_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
-           "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_status_string",
-           "tv_fgp_variant_name")
+           "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_stream_probe",
+           "tv_fgp_status_string", "tv_fgp_variant_name")
 
 
 class TvFgpError(RuntimeError):
@@ -107,6 +107,8 @@ def _load():
     lib.tv_fgp_workspace_bytes.argtypes = [ctypes.c_int, I64, I64, I64]
     lib.tv_fgp_momentum.restype = ctypes.c_float
     lib.tv_fgp_momentum.argtypes = [ctypes.c_int]
+    lib.tv_fgp_stream_probe.restype = ctypes.c_int
+    lib.tv_fgp_stream_probe.argtypes = [P3, P3, I64, P]
     lib.tv_fgp_status_string.restype = ctypes.c_char_p
     lib.tv_fgp_status_string.argtypes = [ctypes.c_int]
     lib.tv_fgp_variant_name.restype = ctypes.c_char_p
@@ -426,3 +428,20 @@ def tv_primal_h(b, p, z, lam, stream=None, dims=None):
     st = lib.tv_primal_h(_addr(b), _hfield(p, shape, "p"), _addr(z), float(lam), nx, ny, nz,
                          _stream(stream))
     _raise(st, "tv_primal_h")
+
+
+def tv_fgp_stream_probe(src, dst, stream=None):
+    """dst[k] = src[k] + src[6] for k < 6: the 7-read / 6-write traffic of one
+    step as a linear stream (a bandwidth ceiling, not a step).  src: 7 float32
+    device tensors, dst: 6, all contiguous with the same number of elements."""
+    if len(src) != 7 or len(dst) != 6:
+        raise ValueError("tv_fgp_stream_probe takes 7 sources and 6 destinations")
+    n = src[0].numel()
+    for t in list(src) + list(dst):
+        _check_dev(t, "probe volume", "float32", n)
+        if t.numel() != n:
+            raise ValueError("probe volumes must have the same number of elements")
+    arr_s = (ctypes.c_void_p * 7)(*[t.data_ptr() for t in src])
+    arr_d = (ctypes.c_void_p * 6)(*[t.data_ptr() for t in dst])
+    st = lib.tv_fgp_stream_probe(arr_s, arr_d, n, _stream(stream))
+    _raise(st, "tv_fgp_stream_probe")

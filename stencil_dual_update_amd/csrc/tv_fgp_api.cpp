@@ -825,6 +825,19 @@ int tv_fgp_solve(const float *b, float *const p[3], float *const r_a[3],
   return TV_OK;
 }
 
+int tv_fgp_stream_probe(const float *const src[7], float *const dst[6], int64_t n,
+                        void *stream) {
+  if (src == nullptr || dst == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(n, 1, 1);
+  if (bytes == 0) return TV_ERR_DIMS;
+  Buf bufs[13];
+  for (int k = 0; k < 7; ++k) bufs[k] = Buf{src[k], bytes, 16, false};
+  for (int k = 0; k < 6; ++k) bufs[7 + k] = Buf{dst[k], bytes, 16, true};
+  const int st = check_buffers(bufs, 13);
+  if (st != TV_OK) return st;
+  return launch_status(tvfgp::launch_stream13(src, dst, n, stream));
+}
+
 size_t tv_fgp_workspace_bytes(int variant, int64_t nx, int64_t ny, int64_t nz) {
   if (!known_variant(variant)) return 0;
   return run_workspace_bytes(variant, volume_bytes(nx, ny, nz));

@@ -144,5 +144,9 @@ int launch_primal_h(const PrimalArgsH &a);
 int launch_duality_gap(const GapArgs &a);
 // Partial triples the gap reduction writes for these dimensions.
 int gap_partial_count(int64_t nx, int64_t ny, int64_t nz);
+// Bandwidth probe: dst[k][i] = src[k][i] + src[6][i] for k < 6 over n
+// elements (the 7-read / 6-write traffic of one step as a linear stream).
+// The volumes must be 16-byte aligned.
+int launch_stream13(const float *const src[7], float *const dst[6], int64_t n, void *stream);
 
 }  // namespace tvfgp

@@ -415,3 +415,30 @@ def test_run2_h_workspace():
                            field(7, 8, 9), 0.01, 0, 3, NX, NY, NZ, None, None) == tvf.TV_ERR_ALIAS
     assert run2_h(addr(9))[0] == tvf.TV_ERR_ALIAS   # first volume is r_b[2]
     assert run2_h(addr(10) + 1)[0] == tvf.TV_ERR_ALIGN
+
+
+def probe(src=tuple(range(7)), dst=tuple(range(7, 13)), n=200):
+    """tv_fgp_stream_probe on fake volumes (k < 1000: the k-th fake volume,
+    else a raw address); only calls that fail validation are made."""
+    def arr(ks, count):
+        if ks is None:
+            return None
+        return (ctypes.c_void_p * count)(*[None if k is None else addr(k) if k < 1000 else k
+                                            for k in ks])
+    return L.tv_fgp_stream_probe(arr(src, 7), arr(dst, 6), n, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(src=None), tvf.TV_ERR_NULL),
+    (dict(dst=None), tvf.TV_ERR_NULL),
+    (dict(src=(0, 1, 2, None, 4, 5, 6)), tvf.TV_ERR_NULL),
+    (dict(n=0), tvf.TV_ERR_DIMS),
+    (dict(n=-5), tvf.TV_ERR_DIMS),
+    (dict(n=1 << 62), tvf.TV_ERR_DIMS),
+    (dict(src=(0, 1, 2, 3, 4, 5, addr(6) + 4)), tvf.TV_ERR_ALIGN),
+    (dict(dst=(7, 8, 9, 10, 11, addr(12) + 8)), tvf.TV_ERR_ALIGN),
+    (dict(dst=(7, 8, 9, 10, 11, 3)), tvf.TV_ERR_ALIAS),   # a dst is a src
+    (dict(dst=(7, 8, 9, 10, 10, 12)), tvf.TV_ERR_ALIAS),  # two dst alias
+])
+def test_stream_probe_rejects(kw, code):
+    assert probe(**kw) == code

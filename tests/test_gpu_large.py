@@ -3,13 +3,15 @@
 1400 x 1300 x 1200 = 2.18e9 voxels, 8.7 GB per volume.  At this size the
 default kernel switches from 32-bit to 64-bit byte offsets, the ablation
 kernels from int32 to int64 indices, and the grid is smaller than the tile
-count, so workgroups loop over tiles.  Each variant runs two steps; sampled
-voxels (corners, faces, interior, tile and group edges) are compared with the
-CPU oracle on sub-boxes of the inputs (after K steps a voxel depends only on
-inputs within K voxels of it).  The duality-gap reduction is checked on the
-same volume against the oracle's gap of the whole volume, and the binary16
-runs (one and two steps per pass) on sampled voxels against the oracle's half
-mode.
+count, so workgroups loop over tiles.  Each variant runs three steps, so the
+three-steps-per-pass run takes one three-step pass (and the two-steps-per-pass
+run one two-step pass and one single step); sampled voxels (corners, faces,
+interior, tile, slab and group edges, offsets past 4 GiB) are compared with
+the CPU oracle on sub-boxes of the inputs (after K steps a voxel depends only
+on inputs within K voxels of it, so a margin of K + 1 is exact).  The
+duality-gap reduction is checked on the same volume against the oracle's gap
+of the whole volume, and the binary16 runs (one and two steps per pass) on
+sampled voxels against the oracle's half mode.
 """
 import numpy as np
 import pytest
@@ -42,22 +44,28 @@ def test_volume_past_2_31_voxels_all_variants():
     rb = torch.empty_like(p)
     ws3 = torch.empty_like(p)  # second p of the two-steps-per-pass variant
     ws = ws3[0]                 # z of the two-kernel variant, then the read-out
+    # slabs of the multi-step kernels start at multiples of 96 or 32 planes,
+    # tiles at multiples of 64 x 8; byte offsets pass 2^32 from plane 591 on
     pts = [(0, 0, 0), (nz - 1, ny - 1, nx - 1), (nz // 2, ny // 2, nx // 2), (7, 1299, 0),
            (1199, 0, 1399), (600, 8 * 81, 64 * 16), (601, 8 * 81 - 1, 64 * 16 - 1),
-           (1100, 517, 1023), (3, 4, 1024), (1196, 1297, 700)]
+           (1100, 517, 1023), (3, 4, 1024), (1196, 1297, 700), (95, 7, 63), (96, 8, 64),
+           (97, 9, 65), (1151, 1295, 1343), (1152, 1296, 1344), (1153, 1297, 1345),
+           (767, 640, 1), (768, 639, 1398), (590, 1299, 1399), (591, 0, 0)]
+    K = 3
     expected = {}
     for c in pts:
-        lo = [max(v - 3, 0) for v in c]
-        hi = [min(v + 4, s) for v, s in zip(c, (nz, ny, nx))]
+        lo = [max(v - K - 1, 0) for v in c]
+        hi = [min(v + K + 2, s) for v, s in zip(c, (nz, ny, nx))]
         sub = np.ascontiguousarray(b[lo[0]:hi[0], lo[1]:hi[1], lo[2]:hi[2]])
         p0 = np.zeros((3,) + sub.shape, np.float32)
-        pe, re, ze = oracle.run_cone(sub, p0, p0, LAM, 1, 2,
+        pe, re, ze = oracle.run_cone(sub, p0, p0, LAM, 1, K,
                                      (c[0] - lo[0], c[1] - lo[1], c[2] - lo[2]))
         expected[c] = (pe, re, ze)
     for variant, v in tvf.VARIANTS.items():
+        print("2.18e9 voxels: %s, %d steps" % (variant, K), flush=True)
         p.zero_()
         ra.zero_()
-        where = tvf.tv_fgp_run(bt, p, ra, rb, LAM, 1, 2, variant=v,
+        where = tvf.tv_fgp_run(bt, p, ra, rb, LAM, 1, K, variant=v,
                                z_ws=ws if v == tvf.TWO_KERNEL else
                                ws3 if v in (tvf.TB2, tvf.TB3) else None)
         r = rb if where else ra
