@@ -15,8 +15,10 @@
  * reference).  Build with -O2 -ffp-contract=off and no fast-math so that
  * each operation is one IEEE-754 round-to-nearest operation.
  *
- * OpenMP splits the outer z loop only.  No loop carries a reduction, so the
- * result does not depend on the number of threads.
+ * OpenMP splits the outer z loop only, and only on volumes of at least
+ * TV_ORACLE_PAR_MIN voxels (on smaller ones starting the threads costs more
+ * than the loop).  No loop carries a reduction, so the result does not depend
+ * on the number of threads.
  */
 #include <math.h>
 #include <stdint.h>
@@ -25,6 +27,8 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+#define TV_ORACLE_PAR_MIN ((int64_t)1 << 15)
 
 /*
  * Momentum coefficient of the k-th step of an outer iteration (k >= 1).
@@ -193,7 +197,7 @@ int tv_oracle_run_h(const float *b, uint16_t *p0, uint16_t *p1, uint16_t *p2,
         for (int k = 1; k <= n_inner; ++k) {
             const float m = (float)tv_oracle_momentum(k);
             for (int a = 0; a < 3; ++a) {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= TV_ORACLE_PAR_MIN)
                 for (int64_t i = 0; i < n; ++i) {
                     pf[a][i] = tv_oracle_f16_to_f32(ph[a][i]);
                     rf[a][i] = tv_oracle_f16_to_f32(rh[a][i]);
@@ -205,7 +209,7 @@ int tv_oracle_run_h(const float *b, uint16_t *p0, uint16_t *p1, uint16_t *p2,
                 return -1;
             }
             for (int a = 0; a < 3; ++a) {
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (n >= TV_ORACLE_PAR_MIN)
                 for (int64_t i = 0; i < n; ++i) {
                     ph[a][i] = tv_oracle_f32_to_f16(pf[a][i]);
                     rh[a][i] = tv_oracle_f32_to_f16(rn[a][i]);

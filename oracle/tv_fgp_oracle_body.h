@@ -27,7 +27,7 @@ static void FN(tv_oracle_L)(const REAL *r0, const REAL *r1, const REAL *r2,
 {
     const int64_t sy = nx, sz = nx * ny;
     int64_t z;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (nx * ny * nz >= TV_ORACLE_PAR_MIN)
     for (z = 0; z < nz; ++z) {
         for (int64_t y = 0; y < ny; ++y) {
             for (int64_t x = 0; x < nx; ++x) {
@@ -53,7 +53,7 @@ static void FN(tv_oracle_D)(const REAL *zv, REAL *g0, REAL *g1, REAL *g2,
 {
     const int64_t sy = nx, sz = nx * ny;
     int64_t z;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (nx * ny * nz >= TV_ORACLE_PAR_MIN)
     for (z = 0; z < nz; ++z) {
         for (int64_t y = 0; y < ny; ++y) {
             for (int64_t x = 0; x < nx; ++x) {
@@ -79,7 +79,7 @@ static void FN(tv_oracle_primal)(const REAL *b, const REAL *r0, const REAL *r1,
     const int64_t n = nx * ny * nz;
     int64_t j;
     FN(tv_oracle_L)(r0, r1, r2, zout, nx, ny, nz);
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (nx * ny * nz >= TV_ORACLE_PAR_MIN)
     for (j = 0; j < n; ++j) {
         const REAL u = b[j] - lam * zout[j];
         zout[j] = (u > (REAL)0) ? u : (REAL)0;
@@ -103,7 +103,7 @@ static void FN(tv_oracle_dual_step)(const REAL *zv, REAL *p0, REAL *p1, REAL *p2
 {
     const int64_t sy = nx, sz = nx * ny;
     int64_t z;
-#pragma omp parallel for schedule(static)
+#pragma omp parallel for schedule(static) if (nx * ny * nz >= TV_ORACLE_PAR_MIN)
     for (z = 0; z < nz; ++z) {
         for (int64_t y = 0; y < ny; ++y) {
             for (int64_t x = 0; x < nx; ++x) {

@@ -114,6 +114,226 @@ __device__ __forceinline__ void tb3_init_extra(Tb3Extra &e, int lx, int ly) {
   e.pr1a = e.pr1b = Tb3Six{0, 0, 0};
 }
 
+// LDS of a workgroup: the rings of the three primals and of the step-one and
+// step-two r (z components two planes deep, x and y one plane).
+struct Tb3Lds {
+  float z0r[2][kT3R0Y][kT3R0X];    // z0 at (x+2, y+2)
+  float r1x[kT3E1Y][kT3E1X];       // r1_x at (x+2, y+2)
+  float r1y[kT3E1Y][kT3E1X];       // r1_y
+  float r1z[2][kT3E1Y][kT3E1X];    // r1_z, two planes
+  float z1r[2][kT3R1Y][kT3R1X];    // z1 at (x+1, y+1)
+  float r2x[kT3E2Y][kT3E2X];       // r2_x at (x+1, y+1)
+  float r2y[kT3E2Y][kT3E2X];       // r2_y
+  float r2z[2][kT3E2Y][kT3E2X];    // r2_z, two planes
+  float z2r[2][kT3R2Y][kT3R2X];    // z2 at (x, y)
+};
+
+// A tile whose R0 lies inside the volume with a voxel to spare on every x
+// and y face: every point of it has lower and upper neighbours in x and y,
+// so the boundary rules in x and y are the identity there.
+template <typename I, typename Off>
+__device__ __forceinline__ bool tb3_interior(I x0, I y0, const ZxGeometry<I, Off> &g) {
+  return x0 >= 3 && y0 >= 3 && x0 + (kT3R0X - 2) < g.nx && y0 + (kT3R0Y - 2) < g.ny;
+}
+
+// The z march of one tile (x0, y0) over the planes [z0, z1).  kInterior:
+// the tile passes tb3_interior, so the x and y boundary flags are constant
+// true and their selects fold away.
+template <bool kInterior, typename I, typename Off, typename S>
+__device__ __forceinline__ void tb3_tile(
+    Tb3Lds &L, const float *__restrict__ b, const S *__restrict__ pi0,
+    const S *__restrict__ pi1, const S *__restrict__ pi2, S *__restrict__ po0,
+    S *__restrict__ po1, S *__restrict__ po2, const S *__restrict__ ri0,
+    const S *__restrict__ ri1, const S *__restrict__ ri2, S *__restrict__ ro0,
+    S *__restrict__ ro1, S *__restrict__ ro2, float lam, float c, float m1, float m2,
+    float m3, const ZxGeometry<I, Off> &g, int tid, bool has_halo, int hlx, int hly, I x0,
+    I y0, I z0, I z1) {
+  const Off sy4 = g.sy4, sz4 = g.sz4;
+  TbPoint<Off> own, hal;
+  tb_init_point<I, Off>(own, tid % kTbTileX, tid / kTbTileX, x0, y0, g);
+  tb_init_point<I, Off>(hal, hlx, hly, x0, y0, g);
+  hal.ok = hal.ok && has_halo;
+  if constexpr (kInterior) {
+    own.ok = true;
+    own.low_x = own.low_y = own.has_x = own.has_y = true;
+    hal.ok = has_halo;
+    hal.low_x = hal.low_y = hal.has_x = hal.has_y = true;
+  }
+  Tb3Extra ox, hx;
+  tb3_init_extra(ox, own.lx, own.ly);
+  tb3_init_extra(hx, hal.lx, hal.ly);
+  // own p2, r2 of planes k and k+1 (step two at the thread's tile point)
+  Tb3Six pra{0, 0, 0}, prb{0, 0, 0};
+
+  const I kstart = z0 - 7;
+  // planes whose inputs the slab reads: [z0 - 2, z1 + 2] (and r_z of z0 - 3)
+  const I lo_in = z0 - 2, hi_in = z1 + 2;
+  auto input_plane = [&](I kp) { return kp >= 0 && kp < g.nz && kp >= lo_in && kp <= hi_in; };
+  if (z0 - 3 >= 0) {
+    const Off j = (Off)(z0 - 3) * sz4;
+    own.q2 = lds(ri2, own.o + j);
+    if (has_halo) hal.q2 = lds(ri2, hal.o + j);
+  }
+  if (input_plane(z0 - 2)) {
+    tb_load<S, Off>(own, (Off)(z0 - 2) * sz4, sy4, b, ri0, ri1, ri2);
+    if (has_halo) tb_load<S, Off>(hal, (Off)(z0 - 2) * sz4, sy4, b, ri0, ri1, ri2);
+  }
+  tb_take(own);
+  tb_take(hal);
+
+  for (I k = kstart; k < z1; ++k) {
+    const I kd1 = k + 4;  // step-one plane
+    const bool do_d1 = kd1 >= z0 - 2 && kd1 >= 0 && kd1 < g.nz && kd1 <= z1 + 1;
+    const I kd2 = k + 2;  // step-two plane
+    const bool do_d2 = kd2 >= z0 - 1 && kd2 >= 0 && kd2 < g.nz && kd2 <= z1;
+    const I kb = k + 5;   // z0 plane
+    const bool do_b = input_plane(kb);
+    const I kf1 = k + 3;  // z1 plane
+    const bool do_f1 = kf1 >= z0 - 1 && kf1 >= 0 && kf1 < g.nz && kf1 <= z1 + 1;
+    const I kf2 = k + 1;  // z2 plane
+    const bool do_f2 = kf2 >= z0 && kf2 < g.nz && kf2 <= z1;
+    const bool do_h = k >= z0;
+    // p_in of the step-one plane
+    if (do_d1) {
+      const Off j = (Off)kd1 * sz4;
+      own.pp0 = lds(pi0, own.o + j);
+      own.pp1 = lds(pi1, own.o + j);
+      own.pp2 = lds(pi2, own.o + j);
+      if (has_halo) {
+        hal.pp0 = lds(pi0, hal.o + j);
+        hal.pp1 = lds(pi1, hal.o + j);
+        hal.pp2 = lds(pi2, hal.o + j);
+      }
+    }
+    // inputs of plane k+6, consumed next iteration
+    const I kl = k + 6;
+    if (input_plane(kl)) {
+      tb_load<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+      if (has_halo) tb_load<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+    }
+
+    // ---- phase 1: z2 of plane k+1 on R2, z1 of plane k+3 on R1, z0 of
+    // plane k+5 on R0.  Every index is inside its array (the lower
+    // neighbours of R2 lie in E2, those of R1 in E1), so the reads are
+    // unconditional and the boundary rule is a select.
+    auto phase_f2 = [&](TbPoint<Off> &pt, const Tb3Extra &e) {
+      const int x = pt.lx + 1, y = pt.ly + 1;
+      const int s = (int)(kf2 & 1), sp = (int)((kf2 + 1) & 1);
+      const float rx = L.r2x[y][x], ry = L.r2y[y][x], rz = L.r2z[s][y][x];
+      const float rxm = L.r2x[y][x - 1], rym = L.r2y[y - 1][x], rzm = L.r2z[sp][y][x];
+      L.z2r[s][pt.ly][pt.lx] = primal_z(e.b1, rx, pt.low_x ? rxm : 0.0f, ry,
+                                        pt.low_y ? rym : 0.0f, rz, kf2 > 0 ? rzm : 0.0f, lam);
+    };
+    auto phase_f1 = [&](TbPoint<Off> &pt) {
+      const int x = pt.lx + 2, y = pt.ly + 2;
+      const int s = (int)(kf1 & 1), sp = (int)((kf1 + 1) & 1);
+      const float rx = L.r1x[y][x], ry = L.r1y[y][x], rz = L.r1z[s][y][x];
+      const float rxm = L.r1x[y][x - 1], rym = L.r1y[y - 1][x], rzm = L.r1z[sp][y][x];
+      L.z1r[s][pt.ly + 1][pt.lx + 1] =
+          primal_z(pt.bqq, rx, pt.low_x ? rxm : 0.0f, ry, pt.low_y ? rym : 0.0f, rz,
+                   kf1 > 0 ? rzm : 0.0f, lam);
+    };
+    auto phase_b = [&](TbPoint<Off> &pt) {
+      L.z0r[kb & 1][pt.ly + 2][pt.lx + 2] =
+          primal_z(pt.cb, pt.c0, pt.low_x ? pt.c0l : 0.0f, pt.c1,
+                   pt.low_y ? pt.c1l : 0.0f, pt.c2, kb > 0 ? pt.q2 : 0.0f, lam);
+    };
+    if (do_f2) {
+      if (own.ok) phase_f2(own, ox);
+      if (hal.ok && hx.r2) phase_f2(hal, hx);
+    }
+    if (do_f1) {
+      if (own.ok) phase_f1(own);
+      if (hal.ok && hx.r1) phase_f1(hal);
+    }
+    if (do_b) {
+      if (own.ok) phase_b(own);
+      if (hal.ok) phase_b(hal);
+    }
+    __syncthreads();
+
+    // ---- phase 2: step three at plane k (tile), step two at plane k+2
+    // (E2), step one at plane k+4 (E1)
+    if (do_h && own.ok) {
+      const int s = (int)(k & 1), sn = (int)((k + 1) & 1);
+      const int x = own.lx, y = own.ly;
+      const float zi = L.z2r[s][y][x], zx = L.z2r[s][y][x + 1], zy = L.z2r[s][y + 1][x];
+      const float zz = L.z2r[sn][y][x];
+      float o0, o1, o2;
+      float pa0 = tb3_lo(pra.a), pa1 = tb3_hi(pra.a), pa2 = tb3_lo(pra.b);
+      dual_update(zi, zx, zy, zz, own.has_x, own.has_y, k + 1 < g.nz, tb3_hi(pra.b),
+                  tb3_lo(pra.c), tb3_hi(pra.c), pa0, pa1, pa2, c, m3, o0, o1, o2);
+      const Off j = own.o + (Off)k * sz4;
+      sts_stream(po0, j, pa0);
+      sts_stream(po1, j, pa1);
+      sts_stream(po2, j, pa2);
+      sts_stream(ro0, j, o0);
+      sts_stream(ro1, j, o1);
+      sts_stream(ro2, j, o2);
+    }
+    pra = prb;
+    // step two at an E2 point from its step-one p1, r1 of plane k+2
+    auto phase_d2 = [&](TbPoint<Off> &pt, Tb3Extra &e, Tb3Six &out) {
+      const int x = pt.lx + 1, y = pt.ly + 1;
+      const int s = (int)(kd2 & 1), sn = (int)((kd2 + 1) & 1);
+      const float zi = L.z1r[s][y][x], zx = L.z1r[s][y][x + 1], zy = L.z1r[s][y + 1][x];
+      const float zz = L.z1r[sn][y][x];
+      float p0o = tb3_lo(e.pr1a.a), p1o = tb3_hi(e.pr1a.a), p2o = tb3_lo(e.pr1a.b);
+      float r0o, r1o, r2o;
+      dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd2 + 1 < g.nz, tb3_hi(e.pr1a.b),
+                  tb3_lo(e.pr1a.c), tb3_hi(e.pr1a.c), p0o, p1o, p2o, c, m2, r0o, r1o, r2o);
+      p0o = as_stored<S>(p0o);
+      p1o = as_stored<S>(p1o);
+      p2o = as_stored<S>(p2o);
+      r0o = as_stored<S>(r0o);
+      r1o = as_stored<S>(r1o);
+      r2o = as_stored<S>(r2o);
+      L.r2x[y][x] = r0o;
+      L.r2y[y][x] = r1o;
+      L.r2z[s][y][x] = r2o;
+      out = tb3_six(p0o, p1o, p2o, r0o, r1o, r2o);
+    };
+    if (do_d2) {
+      if (own.ok) phase_d2(own, ox, prb);
+      if (hal.ok && hx.e2) {
+        Tb3Six unused;
+        phase_d2(hal, hx, unused);
+      }
+    }
+    ox.pr1a = ox.pr1b;
+    hx.pr1a = hx.pr1b;
+    // step one at an E1 point from the input r and p of plane k+4
+    auto phase_d1 = [&](TbPoint<Off> &pt, Tb3Extra &e) {
+      const int x = pt.lx + 2, y = pt.ly + 2;
+      const int s = (int)(kd1 & 1), sn = (int)((kd1 + 1) & 1);
+      const float zi = L.z0r[s][y][x], zx = L.z0r[s][y][x + 1], zy = L.z0r[s][y + 1][x];
+      const float zz = L.z0r[sn][y][x];
+      float r0o, r1o, r2o;
+      dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd1 + 1 < g.nz, pt.q0, pt.q1, pt.q2,
+                  pt.pp0, pt.pp1, pt.pp2, c, m1, r0o, r1o, r2o);
+      r0o = as_stored<S>(r0o);
+      r1o = as_stored<S>(r1o);
+      r2o = as_stored<S>(r2o);
+      e.pr1b = tb3_six(as_stored<S>(pt.pp0), as_stored<S>(pt.pp1), as_stored<S>(pt.pp2), r0o,
+                       r1o, r2o);
+      L.r1x[y][x] = r0o;
+      L.r1y[y][x] = r1o;
+      L.r1z[s][y][x] = r2o;
+    };
+    if (do_d1) {
+      if (own.ok) phase_d1(own, ox);
+      if (hal.ok && hx.e1) phase_d1(hal, hx);
+    }
+    __syncthreads();
+    ox.b1 = ox.b2;
+    ox.b2 = own.bqq;
+    hx.b1 = hx.b2;
+    hx.b2 = hal.bqq;
+    tb_rotate(own);
+    tb_rotate(hal);
+  }
+}
+
 // Four waves per SIMD (two workgroups per CU): the carried state of three
 // levels takes 125 VGPRs; capping at six waves spilled 53 and ran 2.8x slower.
 template <typename I, typename Off, typename S>
@@ -125,15 +345,7 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
     const S *__restrict__ ri2, S *__restrict__ ro0, S *__restrict__ ro1,
     S *__restrict__ ro2, float lam, float c, float m1, float m2, float m3,
     ZxGeometry<I, Off> g) {
-  __shared__ float z0r[2][kT3R0Y][kT3R0X];    // z0 at (x+2, y+2)
-  __shared__ float r1x[kT3E1Y][kT3E1X];       // r1_x at (x+2, y+2)
-  __shared__ float r1y[kT3E1Y][kT3E1X];       // r1_y
-  __shared__ float r1z[2][kT3E1Y][kT3E1X];    // r1_z, two planes
-  __shared__ float z1r[2][kT3R1Y][kT3R1X];    // z1 at (x+1, y+1)
-  __shared__ float r2x[kT3E2Y][kT3E2X];       // r2_x at (x+1, y+1)
-  __shared__ float r2y[kT3E2Y][kT3E2X];       // r2_y
-  __shared__ float r2z[2][kT3E2Y][kT3E2X];    // r2_z, two planes
-  __shared__ float z2r[2][kT3R2Y][kT3R2X];    // z2 at (x, y)
+  __shared__ Tb3Lds L;
   const int tid = (int)threadIdx.x;
   const bool has_halo = tid < kT3Halo;
   int hlx = 0, hly = 0;
@@ -142,7 +354,6 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
   // 7, so they issue first (1% at 512^3).  The branch is on a scalar, so the
   // priority instruction runs in those waves only.
   if (hw_wave_uniform(tid) < kT3Halo) hw_raise_priority();
-  const Off sy4 = g.sy4, sz4 = g.sz4;
 
   for (I t = (I)blockIdx.x; t < g.ntiles; t += (I)gridDim.x) {
     I tx, ty, tz;
@@ -150,183 +361,14 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
     const I x0 = tx * kTbTileX, y0 = ty * kTbTileY;
     const I z0 = tz * g.planes;
     const I z1 = (z0 + g.planes < g.nz) ? z0 + g.planes : g.nz;
-    TbPoint<Off> own, hal;
-    tb_init_point<I, Off>(own, tid % kTbTileX, tid / kTbTileX, x0, y0, g);
-    tb_init_point<I, Off>(hal, hlx, hly, x0, y0, g);
-    hal.ok = hal.ok && has_halo;
-    Tb3Extra ox, hx;
-    tb3_init_extra(ox, own.lx, own.ly);
-    tb3_init_extra(hx, hal.lx, hal.ly);
-    // own p2, r2 of planes k and k+1 (step two at the thread's tile point)
-    Tb3Six pra{0, 0, 0}, prb{0, 0, 0};
-
-    const I kstart = z0 - 7;
-    // planes whose inputs the slab reads: [z0 - 2, z1 + 2] (and r_z of z0 - 3)
-    const I lo_in = z0 - 2, hi_in = z1 + 2;
-    auto input_plane = [&](I kp) { return kp >= 0 && kp < g.nz && kp >= lo_in && kp <= hi_in; };
-    if (z0 - 3 >= 0) {
-      const Off j = (Off)(z0 - 3) * sz4;
-      own.q2 = lds(ri2, own.o + j);
-      if (has_halo) hal.q2 = lds(ri2, hal.o + j);
-    }
-    if (input_plane(z0 - 2)) {
-      tb_load<S, Off>(own, (Off)(z0 - 2) * sz4, sy4, b, ri0, ri1, ri2);
-      if (has_halo) tb_load<S, Off>(hal, (Off)(z0 - 2) * sz4, sy4, b, ri0, ri1, ri2);
-    }
-    tb_take(own);
-    tb_take(hal);
-
-    for (I k = kstart; k < z1; ++k) {
-      const I kd1 = k + 4;  // step-one plane
-      const bool do_d1 = kd1 >= z0 - 2 && kd1 >= 0 && kd1 < g.nz && kd1 <= z1 + 1;
-      const I kd2 = k + 2;  // step-two plane
-      const bool do_d2 = kd2 >= z0 - 1 && kd2 >= 0 && kd2 < g.nz && kd2 <= z1;
-      const I kb = k + 5;   // z0 plane
-      const bool do_b = input_plane(kb);
-      const I kf1 = k + 3;  // z1 plane
-      const bool do_f1 = kf1 >= z0 - 1 && kf1 >= 0 && kf1 < g.nz && kf1 <= z1 + 1;
-      const I kf2 = k + 1;  // z2 plane
-      const bool do_f2 = kf2 >= z0 && kf2 < g.nz && kf2 <= z1;
-      const bool do_h = k >= z0;
-      // p_in of the step-one plane
-      if (do_d1) {
-        const Off j = (Off)kd1 * sz4;
-        own.pp0 = lds(pi0, own.o + j);
-        own.pp1 = lds(pi1, own.o + j);
-        own.pp2 = lds(pi2, own.o + j);
-        if (has_halo) {
-          hal.pp0 = lds(pi0, hal.o + j);
-          hal.pp1 = lds(pi1, hal.o + j);
-          hal.pp2 = lds(pi2, hal.o + j);
-        }
-      }
-      // inputs of plane k+6, consumed next iteration
-      const I kl = k + 6;
-      if (input_plane(kl)) {
-        tb_load<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
-        if (has_halo) tb_load<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
-      }
-
-      // ---- phase 1: z2 of plane k+1 on R2, z1 of plane k+3 on R1, z0 of
-      // plane k+5 on R0.  Every index is inside its array (the lower
-      // neighbours of R2 lie in E2, those of R1 in E1), so the reads are
-      // unconditional and the boundary rule is a select.
-      auto phase_f2 = [&](TbPoint<Off> &pt, const Tb3Extra &e) {
-        const int x = pt.lx + 1, y = pt.ly + 1;
-        const int s = (int)(kf2 & 1), sp = (int)((kf2 + 1) & 1);
-        const float rx = r2x[y][x], ry = r2y[y][x], rz = r2z[s][y][x];
-        const float rxm = r2x[y][x - 1], rym = r2y[y - 1][x], rzm = r2z[sp][y][x];
-        z2r[s][pt.ly][pt.lx] = primal_z(e.b1, rx, pt.low_x ? rxm : 0.0f, ry,
-                                        pt.low_y ? rym : 0.0f, rz, kf2 > 0 ? rzm : 0.0f, lam);
-      };
-      auto phase_f1 = [&](TbPoint<Off> &pt) {
-        const int x = pt.lx + 2, y = pt.ly + 2;
-        const int s = (int)(kf1 & 1), sp = (int)((kf1 + 1) & 1);
-        const float rx = r1x[y][x], ry = r1y[y][x], rz = r1z[s][y][x];
-        const float rxm = r1x[y][x - 1], rym = r1y[y - 1][x], rzm = r1z[sp][y][x];
-        z1r[s][pt.ly + 1][pt.lx + 1] =
-            primal_z(pt.bqq, rx, pt.low_x ? rxm : 0.0f, ry, pt.low_y ? rym : 0.0f, rz,
-                     kf1 > 0 ? rzm : 0.0f, lam);
-      };
-      auto phase_b = [&](TbPoint<Off> &pt) {
-        z0r[kb & 1][pt.ly + 2][pt.lx + 2] =
-            primal_z(pt.cb, pt.c0, pt.low_x ? pt.c0l : 0.0f, pt.c1,
-                     pt.low_y ? pt.c1l : 0.0f, pt.c2, kb > 0 ? pt.q2 : 0.0f, lam);
-      };
-      if (do_f2) {
-        if (own.ok) phase_f2(own, ox);
-        if (hal.ok && hx.r2) phase_f2(hal, hx);
-      }
-      if (do_f1) {
-        if (own.ok) phase_f1(own);
-        if (hal.ok && hx.r1) phase_f1(hal);
-      }
-      if (do_b) {
-        if (own.ok) phase_b(own);
-        if (hal.ok) phase_b(hal);
-      }
-      __syncthreads();
-
-      // ---- phase 2: step three at plane k (tile), step two at plane k+2
-      // (E2), step one at plane k+4 (E1)
-      if (do_h && own.ok) {
-        const int s = (int)(k & 1), sn = (int)((k + 1) & 1);
-        const int x = own.lx, y = own.ly;
-        const float zi = z2r[s][y][x], zx = z2r[s][y][x + 1], zy = z2r[s][y + 1][x];
-        const float zz = z2r[sn][y][x];
-        float o0, o1, o2;
-        float pa0 = tb3_lo(pra.a), pa1 = tb3_hi(pra.a), pa2 = tb3_lo(pra.b);
-        dual_update(zi, zx, zy, zz, own.has_x, own.has_y, k + 1 < g.nz, tb3_hi(pra.b),
-                    tb3_lo(pra.c), tb3_hi(pra.c), pa0, pa1, pa2, c, m3, o0, o1, o2);
-        const Off j = own.o + (Off)k * sz4;
-        sts_stream(po0, j, pa0);
-        sts_stream(po1, j, pa1);
-        sts_stream(po2, j, pa2);
-        sts_stream(ro0, j, o0);
-        sts_stream(ro1, j, o1);
-        sts_stream(ro2, j, o2);
-      }
-      pra = prb;
-      // step two at an E2 point from its step-one p1, r1 of plane k+2
-      auto phase_d2 = [&](TbPoint<Off> &pt, Tb3Extra &e, Tb3Six &out) {
-        const int x = pt.lx + 1, y = pt.ly + 1;
-        const int s = (int)(kd2 & 1), sn = (int)((kd2 + 1) & 1);
-        const float zi = z1r[s][y][x], zx = z1r[s][y][x + 1], zy = z1r[s][y + 1][x];
-        const float zz = z1r[sn][y][x];
-        float p0o = tb3_lo(e.pr1a.a), p1o = tb3_hi(e.pr1a.a), p2o = tb3_lo(e.pr1a.b);
-        float r0o, r1o, r2o;
-        dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd2 + 1 < g.nz, tb3_hi(e.pr1a.b),
-                    tb3_lo(e.pr1a.c), tb3_hi(e.pr1a.c), p0o, p1o, p2o, c, m2, r0o, r1o, r2o);
-        p0o = as_stored<S>(p0o);
-        p1o = as_stored<S>(p1o);
-        p2o = as_stored<S>(p2o);
-        r0o = as_stored<S>(r0o);
-        r1o = as_stored<S>(r1o);
-        r2o = as_stored<S>(r2o);
-        r2x[y][x] = r0o;
-        r2y[y][x] = r1o;
-        r2z[s][y][x] = r2o;
-        out = tb3_six(p0o, p1o, p2o, r0o, r1o, r2o);
-      };
-      if (do_d2) {
-        if (own.ok) phase_d2(own, ox, prb);
-        if (hal.ok && hx.e2) {
-          Tb3Six unused;
-          phase_d2(hal, hx, unused);
-        }
-      }
-      ox.pr1a = ox.pr1b;
-      hx.pr1a = hx.pr1b;
-      // step one at an E1 point from the input r and p of plane k+4
-      auto phase_d1 = [&](TbPoint<Off> &pt, Tb3Extra &e) {
-        const int x = pt.lx + 2, y = pt.ly + 2;
-        const int s = (int)(kd1 & 1), sn = (int)((kd1 + 1) & 1);
-        const float zi = z0r[s][y][x], zx = z0r[s][y][x + 1], zy = z0r[s][y + 1][x];
-        const float zz = z0r[sn][y][x];
-        float r0o, r1o, r2o;
-        dual_update(zi, zx, zy, zz, pt.has_x, pt.has_y, kd1 + 1 < g.nz, pt.q0, pt.q1, pt.q2,
-                    pt.pp0, pt.pp1, pt.pp2, c, m1, r0o, r1o, r2o);
-        r0o = as_stored<S>(r0o);
-        r1o = as_stored<S>(r1o);
-        r2o = as_stored<S>(r2o);
-        e.pr1b = tb3_six(as_stored<S>(pt.pp0), as_stored<S>(pt.pp1), as_stored<S>(pt.pp2), r0o,
-                         r1o, r2o);
-        r1x[y][x] = r0o;
-        r1y[y][x] = r1o;
-        r1z[s][y][x] = r2o;
-      };
-      if (do_d1) {
-        if (own.ok) phase_d1(own, ox);
-        if (hal.ok && hx.e1) phase_d1(hal, hx);
-      }
-      __syncthreads();
-      ox.b1 = ox.b2;
-      ox.b2 = own.bqq;
-      hx.b1 = hx.b2;
-      hx.b2 = hal.bqq;
-      tb_rotate(own);
-      tb_rotate(hal);
-    }
+    if (tb3_interior<I, Off>(x0, y0, g))
+      tb3_tile<true, I, Off, S>(L, b, pi0, pi1, pi2, po0, po1, po2, ri0, ri1, ri2, ro0, ro1,
+                                ro2, lam, c, m1, m2, m3, g, tid, has_halo, hlx, hly, x0, y0,
+                                z0, z1);
+    else
+      tb3_tile<false, I, Off, S>(L, b, pi0, pi1, pi2, po0, po1, po2, ri0, ri1, ri2, ro0, ro1,
+                                 ro2, lam, c, m1, m2, m3, g, tid, has_halo, hlx, hly, x0, y0,
+                                 z0, z1);
   }
 }
 

@@ -43,20 +43,30 @@ thread_local EmulDim3 threadIdx, blockIdx, gridDim, blockDim;
 
 namespace {
 
+// A workgroup barrier as the hardware's: it waits for the threads that have
+// not yet ended (a thread that returns leaves it).
 struct Barrier {
   std::mutex mu;
   std::condition_variable cv;
   unsigned count = 0, waiting = 0, generation = 0;
+  void release() {
+    waiting = 0;
+    ++generation;
+    cv.notify_all();
+  }
   void wait() {
     std::unique_lock<std::mutex> lock(mu);
     const unsigned gen = generation;
     if (++waiting == count) {
-      waiting = 0;
-      ++generation;
-      cv.notify_all();
+      release();
     } else {
       cv.wait(lock, [&] { return gen != generation; });
     }
+  }
+  void leave() {
+    std::unique_lock<std::mutex> lock(mu);
+    --count;
+    if (waiting > 0 && waiting == count) release();
   }
 };
 
@@ -70,8 +80,8 @@ namespace {
 
 template <typename F>
 void run_grid(unsigned grid, unsigned block, F &&body) {
-  g_barrier.count = block;
   for (unsigned bl = 0; bl < grid; ++bl) {
+    g_barrier.count = block;
     std::vector<std::thread> threads;
     threads.reserve(block);
     for (unsigned th = 0; th < block; ++th) {
@@ -81,6 +91,7 @@ void run_grid(unsigned grid, unsigned block, F &&body) {
         blockIdx = {bl, 0, 0};
         threadIdx = {th, 0, 0};
         body();
+        g_barrier.leave();
       });
     }
     for (auto &t : threads) t.join();

@@ -358,8 +358,11 @@ def test_axis_permutation(oracle_mod):
 
 
 def test_thread_count_independence(oracle_mod):
+    """The loops split the z planes over threads on volumes of at least 2^15
+    voxels; this one (47 x 37 x 23 = 40,000) is above that."""
     import phantoms
-    b, p0, r0 = phantoms.make_inputs(4, dims=(33, 21, 17))
+    b, p0, r0 = phantoms.make_inputs(4, dims=(47, 37, 23))
+    assert b.size >= 1 << 15
     old = oracle_mod.get_threads()
     try:
         oracle_mod.set_threads(1)
