@@ -289,6 +289,28 @@ int tv_fgp_duality_gap(const float *b, const float *const p[3], float lambda,
                        void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * tv_fgp_duality_gap for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same kernels and the same output bits, with the partial
+ * sums kept in a static device array of the library instead of a caller's
+ * workspace.  The array holds 3 * 1024 doubles (24 KiB) on each GPU the
+ * library runs on, from the first such call on that GPU until the process
+ * ends; the reduction never needs more (its first pass runs at most 1024
+ * workgroups at any size), and a size that would is TV_ERR_WORKSPACE.  The
+ * call allocates and frees nothing.  Its device is the current device, which
+ * must be the device of `stream`.  Every call on one GPU shares the array:
+ * calls that overlap on one GPU (on different streams, or from different
+ * threads) race and give wrong results; calls in stream order are safe.  The
+ * first call on a device looks the array up (TV_ERR_LAUNCH if that fails).
+ *   out  [out] device, 3 doubles, 8-byte aligned, as tv_fgp_duality_gap.
+ * Other arguments, errors and overlap rules as tv_fgp_duality_gap.
+ */
+int tv_fgp_duality_gap_noalloc(const float *b, const float *const p[3], float lambda,
+                               int64_t nx, int64_t ny, int64_t nz, double *out,
+                               void *stream);
+
+
+/*
  * The inner loop with a convergence check: outer iterations of n_inner steps
  * (as tv_fgp_run, momentum restarted per outer iteration) until the duality
  * gap of p satisfies G <= tol * P(z) (tv_fgp_duality_gap), or max_outer outer

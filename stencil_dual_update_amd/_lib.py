@@ -38,7 +38,8 @@ VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
 # Names declared in include/tv_fgp.h, in declaration order.
 EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_fgp_step2", "tv_fgp_step3",
            "tv_primal",
-           "tv_fgp_step_h", "tv_fgp_run_h", "tv_fgp_step2_h", "tv_fgp_run2_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap", "tv_fgp_solve",
+           "tv_fgp_step_h", "tv_fgp_run_h", "tv_fgp_step2_h", "tv_fgp_run2_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap",
+           "tv_fgp_duality_gap_noalloc", "tv_fgp_solve",
            "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_stream_probe",
            "tv_fgp_status_string", "tv_fgp_variant_name")
 
@@ -98,6 +99,8 @@ def _load():
     lib.tv_fgp_gap_workspace_bytes.argtypes = [I64, I64, I64]
     lib.tv_fgp_duality_gap.restype = ctypes.c_int
     lib.tv_fgp_duality_gap.argtypes = [P, P3, F, I64, I64, I64, P, P, ctypes.c_size_t, P]
+    lib.tv_fgp_duality_gap_noalloc.restype = ctypes.c_int
+    lib.tv_fgp_duality_gap_noalloc.argtypes = [P, P3, F, I64, I64, I64, P, P]
     lib.tv_fgp_solve.restype = ctypes.c_int
     lib.tv_fgp_solve.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int, ctypes.c_double,
                                  I64, I64, I64, ctypes.c_int, P, P, ctypes.c_size_t, P, P,
@@ -341,6 +344,18 @@ def tv_fgp_duality_gap(b, p, lam, out, workspace, stream=None, dims=None):
                                 ws_bytes if not isinstance(workspace, int) else ws_bytes,
                                 _stream(stream))
     _raise(st, "tv_fgp_duality_gap")
+
+
+def tv_fgp_duality_gap_noalloc(b, p, lam, out, stream=None, dims=None):
+    """tv_fgp_duality_gap without a workspace: the partial sums live in the
+    library's static device array (calls that overlap on one GPU race)."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_dev(out, "out", "float64", 3)
+    st = lib.tv_fgp_duality_gap_noalloc(_addr(b), _field(p, shape, "p"), float(lam), nx, ny,
+                                        nz, _addr(out), _stream(stream))
+    _raise(st, "tv_fgp_duality_gap_noalloc")
 
 
 def tv_fgp_solve(b, p, r_a, r_b, lam, max_outer, n_inner, tol, gap_ws, gap_dev,

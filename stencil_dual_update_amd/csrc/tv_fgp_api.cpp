@@ -767,6 +767,33 @@ int tv_fgp_duality_gap(const float *b, const float *const p[3], float lambda,
   return launch_status(tvfgp::launch_duality_gap(a));
 }
 
+int tv_fgp_duality_gap_noalloc(const float *b, const float *const p[3], float lambda,
+                               int64_t nx, int64_t ny, int64_t nz, double *out,
+                               void *stream) {
+  if (p == nullptr || out == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  if (gap_ws_bytes(nx, ny, nz) > tvfgp::gap_static_capacity_bytes()) return TV_ERR_WORKSPACE;
+  const Buf bufs[5] = {vol(b, bytes, false), vol(p[0], bytes, false), vol(p[1], bytes, false),
+                       vol(p[2], bytes, false), Buf{out, 3 * sizeof(double), sizeof(double), true}};
+  st = check_buffers(bufs, 5);
+  if (st != TV_OK) return st;
+  tvfgp::GapArgs a;
+  a.b = b;
+  for (int k = 0; k < 3; ++k) a.p[k] = p[k];
+  a.lam = lambda;
+  a.nx = nx;
+  a.ny = ny;
+  a.nz = nz;
+  a.out = out;
+  a.partial = nullptr;
+  a.stream = stream;
+  return launch_status(tvfgp::launch_duality_gap_static(a));
+}
+
 int tv_fgp_solve(const float *b, float *const p[3], float *const r_a[3],
                  float *const r_b[3], float lambda, int max_outer, int n_inner,
                  double tol, int64_t nx, int64_t ny, int64_t nz, int variant,

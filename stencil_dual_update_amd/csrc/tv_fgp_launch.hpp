@@ -4,6 +4,7 @@
 // dimensions >= 1, parameters finite.
 #pragma once
 
+#include <stddef.h>
 #include <stdint.h>
 
 namespace tvfgp {
@@ -144,6 +145,11 @@ int launch_primal_h(const PrimalArgsH &a);
 int launch_duality_gap(const GapArgs &a);
 // Partial triples the gap reduction writes for these dimensions.
 int gap_partial_count(int64_t nx, int64_t ny, int64_t nz);
+// launch_duality_gap with a.partial ignored: the partial sums go to a static
+// device array of the library (gap_static_capacity_bytes bytes per device),
+// so nothing is allocated.  Calls that overlap on one device race on it.
+int launch_duality_gap_static(const GapArgs &a);
+size_t gap_static_capacity_bytes();
 // Bandwidth probe: dst[k][i] = src[k][i] + src[6][i] for k < 6 over n
 // elements (the 7-read / 6-write traffic of one step as a linear stream).
 // The volumes must be 16-byte aligned.
