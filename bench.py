@@ -183,6 +183,55 @@ def write_traffic(fetch_csv, write_csv, variant):
     print(json.dumps(rec))
 
 
+# The marching tile shapes (x, y, planes) the page sweeps ("TV solver: the FGP
+# step on the GPU", section "What made the difference").
+MARCH_SWEEP = [(32, 8, 32), (32, 8, 16), (32, 8, 8), (32, 8, 4), (32, 8, 2), (32, 16, 16),
+               (32, 16, 8), (32, 4, 32), (64, 4, 16), (64, 8, 8), (64, 4, 8)]
+
+
+def march_sweep(args, tvf, torch, np, phantoms, dev, dims, lam, n_inner):
+    """ms per step of the LDS z-march kernel at each shape of MARCH_SWEEP: the
+    same state (after --warmup steps of the one-step kernel) for every shape,
+    5 untimed and 20 timed launches each, the median of the launch times."""
+    nx, ny, nz = dims
+    nvox = nx * ny * nz
+    b_host, p0_host, _ = phantoms.make_inputs(args.workload, dims)
+    b = torch.from_numpy(b_host).to(dev)
+    p = torch.from_numpy(p0_host).to(dev)
+    r = p.clone()
+    rn = torch.empty_like(r)
+    stream = torch.cuda.Stream(device=dev)
+    with torch.cuda.stream(stream):
+        for k in range(args.warmup):
+            tvf.tv_fgp_step(b, p, r, rn, lam, tvf.momentum(k % n_inner + 1), stream=stream)
+            r, rn = rn, r
+        torch.cuda.synchronize()
+        p_keep, r_keep = p.clone(), r.clone()
+        rows = []
+        for tx, ty, planes in MARCH_SWEEP:
+            p.copy_(p_keep)
+            r.copy_(r_keep)
+            evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                   for _ in range(25)]
+            for q, (e0, e1) in enumerate(evs):
+                e0.record(stream)
+                tvf.tv_fgp_step_march(b, p, r, rn, lam, tvf.momentum(q % n_inner + 1), tx, ty,
+                                      planes, stream=stream)
+                e1.record(stream)
+                r, rn = rn, r
+            torch.cuda.synchronize()
+            ts = sorted(e0.elapsed_time(e1) for e0, e1 in evs[5:])
+            ms = ts[len(ts) // 2]
+            gbs = 52 * nvox / (ms * 1e-3) / 1e9
+            rows.append({"shape": "%dx%dx%d" % (tx, ty, planes), "ms_per_step": round(ms, 5),
+                         "min_ms": round(ts[0], 5), "max_ms": round(ts[-1], 5),
+                         "gbps": round(gbs, 1), "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)})
+            print(json.dumps(rows[-1]), flush=True)
+    print(json.dumps({"march_sweep": rows, "dims": [nx, ny, nz], "launches_timed": 20,
+                      "device": torch.cuda.get_device_name(dev)}), flush=True)
+    return 0
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -210,6 +259,9 @@ def parse():
     ap.add_argument("--storage", default="f32", choices=["f32", "half"],
                     help="storage of the dual p and r (half: binary16, fused kernel only)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy probe")
+    ap.add_argument("--march-sweep", action="store_true",
+                    help="time the LDS z-march kernel at every tile shape of the page's sweep "
+                         "(one step per launch) instead of the headline run")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: build the traffic record under profiles/ from "
                          "two rocprofv3 --pmc counter_collection.csv files of this bench")
@@ -250,6 +302,9 @@ def main():
               file=sys.stderr)
         return 2
     nvox = nx * ny * nz
+
+    if args.march_sweep:
+        return march_sweep(args, tvf, torch, np, phantoms, dev, (nx, ny, nz), lam, n_inner)
 
     t0 = time.time()
     b_host, p0_host, _ = phantoms.make_inputs(args.workload, (nx, ny, nz))

@@ -131,6 +131,22 @@ int tv_fgp_step_ex(const float *b, float *const p[3],
                    int variant, float *z_ws, void *stream);
 
 /*
+ * One step with the LDS z-marching kernel at a chosen tile shape: the
+ * ablation behind the sweep of marching tile shapes on the page "TV solver:
+ * the FGP step on the GPU" (section "What made the difference").  A workgroup
+ * of tile_x * tile_y threads owns a tile_x x tile_y (x, y) tile and walks
+ * `planes` consecutive z planes, staging two planes of r and of z in LDS.
+ * Same step, arguments and results as tv_fgp_step (bit for bit).
+ *   tile_x, tile_y  32 x 4, 32 x 8, 32 x 16, 64 x 4 or 64 x 8; any other
+ *                   shape is TV_ERR_PARAM
+ *   planes          planes per tile, 1..1024, else TV_ERR_PARAM
+ * The variant TV_FGP_LDS_MARCH is this kernel at 64 x 4 x 8.
+ */
+int tv_fgp_step_march(const float *b, float *const p[3], const float *const r_in[3],
+                      float *const r_out[3], float lambda, float m, int64_t nx, int64_t ny,
+                      int64_t nz, int tile_x, int tile_y, int planes, void *stream);
+
+/*
  * The inner loop of the solver: n_outer outer iterations of n_inner FGP
  * steps ("TV solver: the FGP step on the GPU", opening paragraph: an outer
  * iteration runs tv_inner FGP steps).  The momentum sequence is the FISTA
@@ -308,7 +324,6 @@ int tv_fgp_duality_gap(const float *b, const float *const p[3], float lambda,
 int tv_fgp_duality_gap_noalloc(const float *b, const float *const p[3], float lambda,
                                int64_t nx, int64_t ny, int64_t nz, double *out,
                                void *stream);
-
 
 /*
  * The inner loop with a convergence check: outer iterations of n_inner steps

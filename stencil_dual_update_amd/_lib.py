@@ -36,7 +36,7 @@ VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
             "cube_32x4x4": 11, "tb3": TB3}
 
 # Names declared in include/tv_fgp.h, in declaration order.
-EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_run", "tv_fgp_step2", "tv_fgp_step3",
+EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_step_march", "tv_fgp_run", "tv_fgp_step2", "tv_fgp_step3",
            "tv_primal",
            "tv_fgp_step_h", "tv_fgp_run_h", "tv_fgp_step2_h", "tv_fgp_run2_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap",
            "tv_fgp_duality_gap_noalloc", "tv_fgp_solve",
@@ -73,6 +73,9 @@ def _load():
     lib.tv_fgp_step_ex.restype = ctypes.c_int
     lib.tv_fgp_step_ex.argtypes = [P, P3, P3, P3, F, F, I64, I64, I64,
                                    ctypes.c_int, P, P]
+    lib.tv_fgp_step_march.restype = ctypes.c_int
+    lib.tv_fgp_step_march.argtypes = [P, P3, P3, P3, F, F, I64, I64, I64, ctypes.c_int,
+                                      ctypes.c_int, ctypes.c_int, P]
     lib.tv_fgp_run.restype = ctypes.c_int
     lib.tv_fgp_run.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int,
                                I64, I64, I64, ctypes.c_int, P, P,
@@ -267,6 +270,21 @@ def tv_fgp_step(b, p, r_in, r_out, lam, m, variant=FUSED, z_ws=None,
                             _field(r_out, shape, "r_out"), float(lam), float(m),
                             nx, ny, nz, int(variant), _addr(z_ws), _stream(stream))
     _raise(st, "tv_fgp_step")
+
+
+MARCH_SHAPES = ((32, 4), (32, 8), (32, 16), (64, 4), (64, 8))
+
+
+def tv_fgp_step_march(b, p, r_in, r_out, lam, m, tile_x, tile_y, planes, stream=None,
+                      dims=None):
+    """One step with the LDS z-march kernel on tile_x x tile_y tiles of `planes` planes."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    st = lib.tv_fgp_step_march(_addr(b), _field(p, shape, "p"), _field(r_in, shape, "r_in"),
+                               _field(r_out, shape, "r_out"), float(lam), float(m), nx, ny, nz,
+                               int(tile_x), int(tile_y), int(planes), _stream(stream))
+    _raise(st, "tv_fgp_step_march")
 
 
 def tv_fgp_run(b, p, r_a, r_b, lam, n_outer, n_inner, variant=FUSED, z_ws=None,

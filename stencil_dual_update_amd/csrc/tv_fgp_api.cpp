@@ -342,6 +342,31 @@ int tv_fgp_step_ex(const float *b, float *const p[3],
       b, p, r_in, r_out, lambda, c, m, nx, ny, nz, variant, z_ws, stream)));
 }
 
+int tv_fgp_step_march(const float *b, float *const p[3], const float *const r_in[3],
+                      float *const r_out[3], float lambda, float m, int64_t nx, int64_t ny,
+                      int64_t nz, int tile_x, int tile_y, int planes, void *stream) {
+  if (!tvfgp::march_shape_supported(tile_x, tile_y) || planes < 1 || planes > 1024)
+    return TV_ERR_PARAM;
+  if (p == nullptr || r_in == nullptr || r_out == nullptr) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(nx, ny, nz);
+  if (bytes == 0) return TV_ERR_DIMS;
+  float c = 0.0f;
+  int st = check_lambda(lambda, &c);
+  if (st != TV_OK) return st;
+  if (!isfinite(m)) return TV_ERR_PARAM;
+  const Buf bufs[10] = {vol(b, bytes, false),        vol(p[0], bytes, true),
+                        vol(p[1], bytes, true),      vol(p[2], bytes, true),
+                        vol(r_in[0], bytes, false),  vol(r_in[1], bytes, false),
+                        vol(r_in[2], bytes, false),  vol(r_out[0], bytes, true),
+                        vol(r_out[1], bytes, true),  vol(r_out[2], bytes, true)};
+  st = check_buffers(bufs, 10);
+  if (st != TV_OK) return st;
+  tvfgp::StepArgs a = make_step(b, p, r_in, r_out, lambda, c, m, nx, ny, nz,
+                                tvfgp::kVariantLdsMarch, nullptr, stream);
+  a.planes = planes;
+  return launch_status(tvfgp::launch_lds_march_shape(a, tile_x, tile_y));
+}
+
 int tv_fgp_step(const float *b, float *const p[3], const float *const r_in[3],
                 float *const r_out[3], float lambda, float m, int64_t nx,
                 int64_t ny, int64_t nz, void *stream) {

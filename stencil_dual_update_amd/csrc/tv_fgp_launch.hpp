@@ -138,6 +138,10 @@ int launch_fused_pair_h(const StepArgsH &a);
 int launch_tb2(const Step2Args &a);
 int launch_tb2_h(const Step2ArgsH &a);
 int launch_tb3(const Step3Args &a);
+// LDS z-march with a tile of tile_x x tile_y (32 x 4, 32 x 8, 32 x 16,
+// 64 x 4, 64 x 8) and a.planes planes per tile.
+bool march_shape_supported(int tile_x, int tile_y);
+int launch_lds_march_shape(const StepArgs &a, int tile_x, int tile_y);
 // Cube-tiled ablation, shape chosen by a.variant (kVariantCube...).
 int launch_cube(const StepArgs &a);
 int launch_primal_h(const PrimalArgsH &a);

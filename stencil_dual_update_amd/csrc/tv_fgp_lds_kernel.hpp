@@ -1,17 +1,20 @@
 // LDS z-marching ablation of the FGP step for gfx950.
 //
 // The page "TV solver: the FGP step on the GPU" (table "Variants", and
-// "What made the difference") describes x-y tiles that march along z with two
-// planes of r and of z staged in shared memory.  Here a 64 x 4 tile marches
-// along z (8 planes per tile by default).  At every plane the workgroup
-// stages r of the next plane on the tile grown by its lower x column and
-// lower y row (66 x 6 points, 0 outside the volume: the lower-face rule of L),
-// computes z of the next plane once per point of the tile plus its upper x
-// column and upper y row (65 x 5 points) from the two staged r planes, and
-// then every thread updates its voxel from z(i), z(i+e_x), z(i+e_y) of the
-// current plane, z(i+e_z) of the next one and its own r of the current plane.
-// Three barriers per plane.  The arithmetic is the shared primal_z /
-// dual_update pair, so the result is bit-identical to the other variants.
+// "What made the difference", with its sweep of marching tile shapes)
+// describes x-y tiles that march along z with two planes of r and of z staged
+// in shared memory.  Here a TX x TY tile marches along z (`planes` planes per
+// tile; the default variant is 64 x 4 with 8 planes, and the shapes of the
+// page's sweep, 32 x 4, 32 x 8, 32 x 16, 64 x 4 and 64 x 8, are instantiated
+// for tv_fgp_step_march).  At every plane the workgroup stages r of the next
+// plane on the tile grown by its lower x column and lower y row ((TX+2) x
+// (TY+2) points, 0 outside the volume: the lower-face rule of L), computes z
+// of the next plane once per point of the tile plus its upper x column and
+// upper y row ((TX+1) x (TY+1) points) from the two staged r planes, and then
+// every thread updates its voxel from z(i), z(i+e_x), z(i+e_y) of the current
+// plane, z(i+e_z) of the next one and its own r of the current plane.  Three
+// barriers per plane.  The arithmetic is the shared primal_z / dual_update
+// pair, so the result is bit-identical to the other variants.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,34 +27,46 @@
 
 namespace tvfgp {
 
-constexpr int kZW = kTileX + 1;  // tile width plus the upper x column
-constexpr int kZH = kTileY + 1;  // tile height plus the upper y row
-constexpr int kRW = kTileX + 2;  // lower x column, tile, upper x column
-constexpr int kRH = kTileY + 2;  // lower y row, tile, upper y row
-
+// Tiles of TX x TY for the marching kernel (planes per tile as given).
 template <typename I>
-__global__ __launch_bounds__(kBlock) void lds_march_kernel(
+inline Geometry<I> march_geometry(int64_t nx, int64_t ny, int64_t nz, int64_t planes, int tx,
+                                  int ty) {
+  Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
+  g.tiles_x = (I)((nx + tx - 1) / tx);
+  g.tiles_y = (I)((ny + ty - 1) / ty);
+  g.ntiles = g.tiles_x * g.tiles_y * g.tiles_z;
+  return g;
+}
+
+template <typename I, int TX, int TY>
+__global__ __launch_bounds__(TX * TY) void lds_march_kernel(
     const float *__restrict__ b, float *__restrict__ p0,
     float *__restrict__ p1, float *__restrict__ p2,
     const float *__restrict__ ri0, const float *__restrict__ ri1,
     const float *__restrict__ ri2, float *__restrict__ ro0,
     float *__restrict__ ro1, float *__restrict__ ro2, float lam, float c,
     float m, Geometry<I> g) {
+  constexpr int kB = TX * TY;
+  constexpr int kZW = TX + 1;  // tile width plus the upper x column
+  constexpr int kZH = TY + 1;  // tile height plus the upper y row
+  constexpr int kRW = TX + 2;  // lower x column, tile, upper x column
+  constexpr int kRH = TY + 2;  // lower y row, tile, upper y row
+  static_assert(kB >= TX + TY, "every halo z point needs a thread");
   // r at tile coordinates (x, y) is rbuf[.][.][y + 1][x + 1], z is zbuf[.][y][x]
   __shared__ float rbuf[2][3][kRH][kRW];
   __shared__ float zbuf[2][kZH][kZW];
   const int tid = (int)threadIdx.x;
-  const int lx = tid % kTileX;
-  const int ly = tid / kTileX;
-  // Halo z point of this thread: wave 0 takes the upper y row, lanes 0..3 of
-  // wave 1 the upper x column; other threads have none.
+  const int lx = tid % TX;
+  const int ly = tid / TX;
+  // Halo z point of this thread: threads 0..TX-1 take the upper y row,
+  // threads TX..TX+TY-1 the upper x column; other threads have none.
   int hxl = -1, hyl = -1;
-  if (ly == 0) {
-    hxl = lx;
-    hyl = kTileY;
-  } else if (ly == 1 && lx < kTileY) {
-    hxl = kTileX;
-    hyl = lx;
+  if (tid < TX) {
+    hxl = tid;
+    hyl = TY;
+  } else if (tid < TX + TY) {
+    hxl = TX;
+    hyl = tid - TX;
   }
   const I sy = g.sy, sz = g.sz;
 
@@ -61,7 +76,7 @@ __global__ __launch_bounds__(kBlock) void lds_march_kernel(
     const I rest = tile / g.tiles_x;
     const I ty = rest % g.tiles_y;
     const I tz = rest / g.tiles_y;
-    const I x0 = tx * kTileX, y0 = ty * kTileY;
+    const I x0 = tx * TX, y0 = ty * TY;
     const I z0 = tz * g.planes;
     const I z1 = (z0 + g.planes < g.nz) ? z0 + g.planes : g.nz;
 
@@ -73,7 +88,7 @@ __global__ __launch_bounds__(kBlock) void lds_march_kernel(
 
     // r of plane k on the staged region, 0 outside the volume
     auto stage = [&](int slot, I k) {
-      for (int s = tid; s < kRW * kRH; s += kBlock) {
+      for (int s = tid; s < kRW * kRH; s += kB) {
         const int sx = s % kRW, sy2 = s / kRW;
         const I gx = x0 + sx - 1, gy = y0 + sy2 - 1;
         float v0 = 0.0f, v1 = 0.0f, v2 = 0.0f;

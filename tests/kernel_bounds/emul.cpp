@@ -11,6 +11,7 @@
 // usage: emul <variant> <nx> <ny> <nz> <wide:0|1> <grid:0=as launched> <end_aligned:0|1> <planes>
 //   variant: fused | fused_nostream | fused_h | fused_nostream_h | pair | pair_nostream |
 //            pair_h | pair_nostream_h | reg_march | point | two_kernel | lds_march |
+//            lds_march_32x4 | lds_march_32x8 | lds_march_32x16 | lds_march_64x8 |
 //            primal | primal_h | gap | gap_pair | tb2 | tb2_h | cube | cube_32x8x2 | cube_64x8x1 |
 //            cube_8x8x8 | cube_32x4x4
 //   (the pair variants need an even nx; with an odd one they report "ok" without running)
@@ -83,6 +84,15 @@ unsigned pick_grid(int64_t ntiles, unsigned override_grid) {
 struct Bufs {
   float *b, *p[3], *ri[3], *ro[3], *z, *po[3];
 };
+
+template <typename I, int TX, int TY>
+void run_march(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid, int64_t planes) {
+  const tvfgp::Geometry<I> g = tvfgp::march_geometry<I>(nx, ny, nz, planes, TX, TY);
+  run_grid(pick_grid(g.ntiles, grid), TX * TY, [&] {
+    tvfgp::lds_march_kernel<I, TX, TY>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2],
+                                       v.ro[0], v.ro[1], v.ro[2], 0.01f, 8.3f, 0.5f, g);
+  });
+}
 
 template <typename I, typename Off, typename S>
 void run_tb3(const Bufs &v, int64_t nx, int64_t ny, int64_t nz, unsigned grid, int64_t planes) {
@@ -235,11 +245,15 @@ void run_ablation(const char *variant, const Bufs &v, int64_t nx, int64_t ny, in
     });
     run_grid(1, kGapFinalBlock, [&] { gap_final_kernel(partial, count, 0.01, out); });
   } else if (!strcmp(variant, "lds_march")) {
-    const Geometry<I> g = make_geometry<I>(nx, ny, nz, planes);
-    run_grid(pick_grid(g.ntiles, grid), kBlock, [&] {
-      lds_march_kernel<I>(v.b, v.p[0], v.p[1], v.p[2], v.ri[0], v.ri[1], v.ri[2], v.ro[0],
-                          v.ro[1], v.ro[2], 0.01f, 8.3f, 0.5f, g);
-    });
+    run_march<I, kTileX, kTileY>(v, nx, ny, nz, grid, planes);
+  } else if (!strcmp(variant, "lds_march_32x4")) {
+    run_march<I, 32, 4>(v, nx, ny, nz, grid, planes);
+  } else if (!strcmp(variant, "lds_march_32x8")) {
+    run_march<I, 32, 8>(v, nx, ny, nz, grid, planes);
+  } else if (!strcmp(variant, "lds_march_32x16")) {
+    run_march<I, 32, 16>(v, nx, ny, nz, grid, planes);
+  } else if (!strcmp(variant, "lds_march_64x8")) {
+    run_march<I, 64, 8>(v, nx, ny, nz, grid, planes);
   } else {
     fprintf(stderr, "unknown variant %s\n", variant);
     exit(2);

@@ -11,7 +11,8 @@
 //             [planes: tb2 slab length, 0 = as launched]
 //   kernel: fused  one step (m1), p updated in place
 //           cube, cube_8x8x8  one step (m1) with the cube-tiled kernel
-//           lds_march  one step (m1) with the LDS z-march (8 planes per tile)
+//           lds_march  one step (m1) with the LDS z-march (64 x 4 tiles, 8 planes)
+//           lds_march_<TX>x<TY>  the same with TX x TY tiles (32x4, 32x8, 32x16, 64x8)
 //           gap    duality gap of p (three doubles written to <dir>/gap.bin)
 //           gap_pair  the same with two voxels per lane (even nx)
 //           pair   one step of the two-voxels-per-lane kernel (even nx)
@@ -122,6 +123,18 @@ unsigned pick(int64_t ntiles, unsigned grid) {
   return grid ? grid : tvfgp::grid_for(ntiles);
 }
 
+template <typename I, int TX, int TY>
+void run_march(int64_t nx, int64_t ny, int64_t nz, int64_t planes, unsigned grid,
+               const float *b, float *p, const float *r, float *r_out, float lam, float c,
+               float m) {
+  const size_t n = (size_t)(nx * ny * nz);
+  const tvfgp::Geometry<I> g = tvfgp::march_geometry<I>(nx, ny, nz, planes, TX, TY);
+  run_grid(pick(g.ntiles, grid), TX * TY, [&] {
+    tvfgp::lds_march_kernel<I, TX, TY>(b, p, p + n, p + 2 * n, r, r + n, r + 2 * n, r_out,
+                                       r_out + n, r_out + 2 * n, lam, c, m, g);
+  });
+}
+
 template <typename I, typename Off>
 void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, float m1, float m2,
          float m3,
@@ -202,11 +215,20 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
     }
     fclose(f);
   } else if (!strcmp(kernel, "lds_march")) {
-    const tvfgp::Geometry<I> g = tvfgp::make_geometry<I>(nx, ny, nz, 8);
-    run_grid(pick(g.ntiles, grid), tvfgp::kBlock, [&] {
-      tvfgp::lds_march_kernel<I>(b, p, p + n, p + 2 * n, r, r + n, r + 2 * n, r_out,
-                                 r_out + n, r_out + 2 * n, lam, c, m1, g);
-    });
+    run_march<I, tvfgp::kTileX, tvfgp::kTileY>(nx, ny, nz, planes > 0 ? planes : 8, grid, b, p, r,
+                                               r_out, lam, c, m1);
+    memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "lds_march_32x4")) {
+    run_march<I, 32, 4>(nx, ny, nz, planes > 0 ? planes : 8, grid, b, p, r, r_out, lam, c, m1);
+    memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "lds_march_32x8")) {
+    run_march<I, 32, 8>(nx, ny, nz, planes > 0 ? planes : 8, grid, b, p, r, r_out, lam, c, m1);
+    memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "lds_march_32x16")) {
+    run_march<I, 32, 16>(nx, ny, nz, planes > 0 ? planes : 8, grid, b, p, r, r_out, lam, c, m1);
+    memcpy(p_out, p, 3 * n * sizeof(float));
+  } else if (!strcmp(kernel, "lds_march_64x8")) {
+    run_march<I, 64, 8>(nx, ny, nz, planes > 0 ? planes : 8, grid, b, p, r, r_out, lam, c, m1);
     memcpy(p_out, p, 3 * n * sizeof(float));
   } else if (!strcmp(kernel, "cube")) {
     const auto g = tvfgp::cube_geometry<I, 16, 8, 4>(nx, ny, nz);

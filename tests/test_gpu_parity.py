@@ -432,3 +432,65 @@ def test_workload4_anisotropic_sampled_10_steps(tvf):
         assert np.array_equal(p10[idx].view(np.uint32), pe.view(np.uint32)), c
         assert np.array_equal(r10[idx].view(np.uint32), re.view(np.uint32)), c
         assert z10[c] == ze, c
+
+
+# --------------------------------------------------------------------------
+# the marching kernel at every tile shape of the page's sweep ("TV solver:
+# the FGP step on the GPU", section "What made the difference")
+
+PAGE_MARCH_SHAPES = [(32, 8, 32), (32, 8, 16), (32, 8, 8), (32, 8, 4), (32, 8, 2), (32, 16, 16),
+                     (32, 16, 8), (32, 4, 32), (64, 4, 16), (64, 8, 8), (64, 4, 8)]
+
+
+def march_solve(tvf, b, p0, r0, lam, n_outer, n_inner, shape):
+    """n_outer x n_inner steps with tv_fgp_step_march (momentum restarted per
+    outer iteration, r ping-pong), then the read-out z."""
+    tx, ty, planes = shape
+    dev = torch.device("cuda")
+    bt = torch.from_numpy(np.ascontiguousarray(b)).to(dev)
+    p = torch.from_numpy(np.ascontiguousarray(p0)).to(dev)
+    r = torch.from_numpy(np.ascontiguousarray(r0)).to(dev)
+    rn = torch.full_like(r, float("nan"))
+    for _ in range(n_outer):
+        for k in range(1, n_inner + 1):
+            tvf.tv_fgp_step_march(bt, p, r, rn, lam, tvf.momentum(k), tx, ty, planes)
+            r, rn = rn, r
+    z = torch.empty_like(bt)
+    tvf.tv_primal(bt, p, z, lam)
+    torch.cuda.synchronize()
+    out = p.cpu().numpy(), r.cpu().numpy(), z.cpu().numpy()
+    del bt, p, r, rn, z
+    return out
+
+
+@pytest.mark.parametrize("shape", PAGE_MARCH_SHAPES, ids=lambda s: "%dx%dx%d" % s)
+def test_march_shapes_ragged(tvf, shape):
+    for dims in [(67, 45, 29), (1, 1, 1), (33, 17, 40), (130, 3, 70), (2100, 20, 5)]:
+        b, p0, r0 = phantoms.make_inputs(4, dims)
+        exp = oracle_solve(b, p0, r0, 0.003, 2, 5)
+        got = march_solve(tvf, b, p0, r0, 0.003, 2, 5, shape)
+        label = "march %s %s" % (shape, dims)
+        assert_close(got, exp, label)
+        assert_bitwise(got, exp, label)
+
+
+@pytest.mark.parametrize("idx", [1, 2], ids=["blobs128", "ellipsoids256"])
+def test_march_shapes_full_200_steps(tvf, idx):
+    b, p0, r0, lam, no, ni, exp = reference(idx)
+    for shape in PAGE_MARCH_SHAPES:
+        print("march %s workload %d: %d x %d steps" % (shape, idx, no, ni), flush=True)
+        got = march_solve(tvf, b, p0, r0, lam, no, ni, shape)
+        assert_close(got, exp, "march %s w%d" % (shape, idx))
+        assert_bitwise(got, exp, "march %s w%d" % (shape, idx))
+        del got
+
+
+def test_march_rejects_other_shapes(tvf):
+    b = torch.zeros((4, 5, 6), device="cuda")
+    p = torch.zeros((3, 4, 5, 6), device="cuda")
+    r = torch.zeros_like(p)
+    ro = torch.zeros_like(p)
+    for tx, ty, planes in [(16, 8, 8), (64, 16, 8), (32, 8, 0), (32, 8, 1025)]:
+        with pytest.raises(tvf.TvFgpError) as e:
+            tvf.tv_fgp_step_march(b, p, r, ro, 0.01, 0.0, tx, ty, planes)
+        assert e.value.status == tvf.TV_ERR_PARAM

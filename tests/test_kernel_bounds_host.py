@@ -24,7 +24,8 @@ SHAPES = [(67, 45, 29), (1, 1, 1), (1, 1, 9), (9, 1, 1), (1, 7, 1), (130, 3, 70)
           (1100, 10, 7), (2100, 20, 5), (3, 300, 5), (200, 9, 33), (2, 1, 1), (258, 17, 6),
           (126, 9, 4), (66, 10, 40), (130, 17, 33)]
 VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
-            "pair_h", "pair_nostream_h", "reg_march", "point", "two_kernel", "lds_march", "primal",
+            "pair_h", "pair_nostream_h", "reg_march", "point", "two_kernel", "lds_march", "lds_march_32x4", "lds_march_32x8",
+            "lds_march_32x16", "lds_march_64x8", "primal",
             "primal_h", "gap", "gap_pair", "tb2", "tb2_h", "tb3", "tb3_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8",
             "cube_32x4x4"]
 FOUR_PLANE = ("tb2", "tb2_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8", "cube_32x4x4", "fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",

@@ -115,6 +115,22 @@ def test_lds_one_step(func, tmp_path, kernel, dims):
     assert_bits(rg, re, "r")
 
 
+@pytest.mark.parametrize("kernel,planes", [("lds_march_32x4", 32), ("lds_march_32x8", 2),
+                                           ("lds_march_32x8", 8), ("lds_march_32x16", 16),
+                                           ("lds_march_64x8", 8), ("lds_march", 16)],
+                         ids=lambda c: str(c))
+@pytest.mark.parametrize("dims", [(37, 19, 11), (70, 33, 40), (1, 1, 1)], ids=lambda d: str(d))
+def test_lds_march_shapes_one_step(func, tmp_path, kernel, planes, dims):
+    """The marching kernel at the tile shapes of the page's sweep, one step
+    against the oracle bit for bit (tiles and plane slabs ragged at the faces)."""
+    b, p0, r0 = inputs(dims)
+    pg, rg = emulate(func, tmp_path, kernel, b, p0, r0, 0.003, np.float32(0.4), 0.0,
+                     planes=planes)
+    pe, re = oracle.step(b, p0, r0, 0.003, np.float32(0.4))
+    assert_bits(pg, pe, "p")
+    assert_bits(rg, re, "r")
+
+
 @pytest.mark.parametrize("kernel,dims,grid", [
     ("gap", (67, 19, 11), 0), ("gap", (130, 17, 9), 3), ("gap", (1, 1, 1), 0),
     ("gap_pair", (130, 17, 9), 0), ("gap_pair", (258, 9, 19), 5), ("gap_pair", (2, 1, 1), 0),
