@@ -139,10 +139,18 @@ def _counter_rows(path):
     rows = {}
     with open(path) as f:
         for r in csv.DictReader(f):
-            d = rows.setdefault(r["Dispatch_Id"], {"name": r["Kernel_Name"], "grid": r["Grid_Size"],
-                                                   "value": 0.0})
+            d = rows.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                        "grid": r["Grid_Size"], "value": 0.0})
             d["value"] += float(r["Counter_Value"])
-    return list(rows.values())
+    return [rows[k] for k in sorted(rows)]
+
+
+def probe_copies(rows, value, count):
+    """Counter readings of the 1 GiB copy the counters are scaled by: the last
+    `count` copies (copyBuffer dispatches, in dispatch order) of the run, which
+    are the probe's; torch's copies of p and r come earlier."""
+    copies = [r for r in rows if "copyBuffer" in r["name"]]
+    return [value(r) for r in copies[-count:]]
 
 
 def write_traffic(fetch_csv, write_csv, variant):
@@ -157,7 +165,8 @@ def write_traffic(fetch_csv, write_csv, variant):
     res = {}
     for key, path in (("fetch", fetch_csv), ("write", write_csv)):
         rows = _counter_rows(path)
-        copy = [r["value"] for r in rows if "copyBuffer" in r["name"]]
+        # the copy probe makes the run's last 23 copies (3 untimed, 20 timed)
+        copy = probe_copies(rows, lambda r: r["value"], 23)
         kern = [r["value"] for r in rows if kname in r["name"]]
         if not copy or not kern:
             raise SystemExit("%s: no copy or %s dispatches found" % (path, kname))
@@ -232,6 +241,143 @@ def march_sweep(args, tvf, torch, np, phantoms, dev, dims, lam, n_inner):
     return 0
 
 
+# Variants of the counter table and the kernels each launches (name prefixes
+# as the kernel trace prints them).
+TABLE_VARIANTS = [("fused", ["fused_zx_kernel"]), ("pair", ["fused_pair_kernel"]),
+                  ("point", ["fused_point_kernel"]), ("reg_march", ["fused_march_kernel"]),
+                  ("lds_march", ["lds_march_kernel"]),
+                  ("two_kernel", ["primal_kernel", "dual_kernel"]),
+                  ("cube", ["cube_kernel"]), ("tb2", ["tb2_kernel"]), ("tb3", ["tb3_kernel"])]
+
+
+def variant_table_run(args, tvf, torch, phantoms, dev, dims, lam, n_inner):
+    """Each variant of TABLE_VARIANTS launched 2 + 5 times on the state after
+    --warmup one-step steps (tb2 and tb3 through tv_fgp_step2 / step3), and
+    the 1 GiB copy the counters are scaled by.  For rocprofv3 passes."""
+    b_host, p0_host, _ = phantoms.make_inputs(args.workload, dims)
+    b = torch.from_numpy(b_host).to(dev)
+    p = torch.from_numpy(p0_host).to(dev)
+    r = p.clone()
+    rn = torch.empty_like(r)
+    for k in range(args.warmup):
+        tvf.tv_fgp_step(b, p, r, rn, lam, tvf.momentum(k % n_inner + 1))
+        r, rn = rn, r
+    p_keep, r_keep = p.clone(), r.clone()
+    p_out = torch.empty_like(p)
+    z_ws = torch.empty_like(b)
+    m = [tvf.momentum(k) for k in (2, 3, 4)]
+    for name, _ in TABLE_VARIANTS:
+        p.copy_(p_keep)
+        r.copy_(r_keep)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(7):
+            if name == "tb2":
+                tvf.tv_fgp_step2(b, p, p_out, r, rn, lam, m[0], m[1])
+            elif name == "tb3":
+                tvf.tv_fgp_step3(b, p, p_out, r, rn, lam, *m)
+            else:
+                v = tvf.VARIANTS[name]
+                tvf.tv_fgp_step(b, p, r, rn, lam, m[0], variant=v,
+                                z_ws=z_ws if v == tvf.TWO_KERNEL else None)
+        torch.cuda.synchronize()
+        print("%s: 7 launches, %.1f ms" % (name, (time.perf_counter() - t0) * 1e3), flush=True)
+    src = torch.empty(1 << 28, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print("variant table run done", flush=True)
+    return 0
+
+
+def _per_dispatch(path):
+    """{dispatch id: {"name":..., "grid":..., counter: value}} from a rocprofv3 counter CSV."""
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            d = rows.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"],
+                                                        "grid": r["Grid_Size"]})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    return rows
+
+
+def variant_table(root):
+    """The per-variant counter table (the page's section "Profiler counters",
+    at 512^3) from the rocprofv3 passes over --variant-table-run."""
+    import csv
+    import statistics
+
+    def find(sub, suffix):
+        d = os.path.join(root, sub)
+        for f in sorted(os.listdir(d)):
+            if f.endswith(suffix):
+                return os.path.join(d, f)
+        raise SystemExit("no *%s under %s" % (suffix, d))
+
+    trace = list(csv.DictReader(open(find("trace", "kernel_trace.csv"))))
+    fetch = _per_dispatch(find("fetch", "counter_collection.csv"))
+    write = _per_dispatch(find("write", "counter_collection.csv"))
+    tcc = _per_dispatch(find("tcc", "counter_collection.csv"))
+    occ = _per_dispatch(find("occ", "counter_collection.csv"))
+
+    def kernel_rows(rows, prefix):
+        return [v for k, v in sorted(rows.items()) if _bare(v["name"]) == prefix]
+
+    def scale(rows, counter):
+        # the run ends with the three probe copies
+        copy = probe_copies([rows[k] for k in sorted(rows)], lambda r: r[counter], 3)
+        return (1 << 20) / statistics.median(copy)   # KiB of 1 GiB / reading
+
+    fs, ws = scale(fetch, "FETCH_SIZE"), scale(write, "WRITE_SIZE")
+    nvox = 512 ** 3
+    vol = nvox * 4
+    lines = ["%-11s %-18s %8s %8s %6s %8s %7s %6s %8s %7s %9s %5s %6s %5s" % (
+        "variant", "kernel", "us", "alg GB/s", "% 8TB", "HBM MiB", "volumes", "x alg", "HBM GB/s",
+        "L2 hit", "occupancy", "VGPR", "LDS KB", "waves")]
+    for name, kernels in TABLE_VARIANTS:
+        for kn in kernels:
+            tr = [t for t in trace if _bare(t["Kernel_Name"]) == kn]
+            if not tr:
+                continue
+            dur = [int(t["End_Timestamp"]) - int(t["Start_Timestamp"]) for t in tr][2:]
+            us = statistics.median(dur) / 1e3
+            f_kib = statistics.median([v["FETCH_SIZE"] for v in kernel_rows(fetch, kn)][2:])
+            w_kib = statistics.median([v["WRITE_SIZE"] for v in kernel_rows(write, kn)][2:])
+            hbm = (f_kib * fs + w_kib * ws) * 1024
+            t_rows = kernel_rows(tcc, kn)[2:]
+            hit = statistics.median([v["TCC_HIT_sum"] / max(1.0, v["TCC_HIT_sum"] + v["TCC_MISS_sum"])
+                                     for v in t_rows])
+            o = statistics.median([v["MeanOccupancyPerActiveCU"] for v in kernel_rows(occ, kn)][2:])
+            alg = (20 if kn == "primal_kernel" else 52) * nvox
+            t0 = tr[0]
+            # the trace's VGPR_Count is half the count the code object declares
+            # on this part (e.g. 64 for the three-step kernel's 128)
+            vgpr, agpr = 2 * int(t0["VGPR_Count"]), int(t0["Accum_VGPR_Count"])
+            lds = int(t0["LDS_Block_Size"])
+            wg_waves = (int(t0["Workgroup_Size_X"]) + 63) // 64
+            # waves per SIMD the registers and the LDS allow (512 VGPRs of 64
+            # lanes per SIMD in granules of 8, 160 KiB of LDS per CU of four
+            # SIMDs, at most 8 waves per SIMD)
+            regs = ((vgpr + 3) // 4 * 4 + agpr) if agpr else vgpr
+            by_vgpr = 512 // ((regs + 7) // 8 * 8)
+            by_lds = (160 * 1024 // lds) * wg_waves / 4.0 if lds else 8.0
+            theo = min(8.0, by_vgpr, by_lds)
+            lines.append("%-11s %-18s %8.1f %8.1f %6.1f %8.0f %7.2f %6.2f %8.1f %6.1f%% %4.2f/%-4.1f %5d %6.1f %5d" % (
+                name, kn, us, alg / (us * 1e3), 100 * alg / (us * 1e3) / HBM_PEAK_GBS, hbm / 2 ** 20,
+                hbm / vol, hbm / alg, hbm / (us * 1e3), 100 * hit, o, theo, regs, lds / 1024, wg_waves))
+    print("\n".join(lines))
+    return 0
+
+
+def _bare(name):
+    """Kernel name without 'void ', namespaces and arguments."""
+    n = name.replace("void ", "").replace("tvfgp::(anonymous namespace)::", "")
+    n = n.replace("tvfgp::", "")
+    return n.split("(")[0].split("<")[0] if not n.startswith("at::") else n
+
+
 def cpu_model():
     try:
         with open("/proc/cpuinfo") as f:
@@ -262,6 +408,13 @@ def parse():
     ap.add_argument("--march-sweep", action="store_true",
                     help="time the LDS z-march kernel at every tile shape of the page's sweep "
                          "(one step per launch) instead of the headline run")
+    ap.add_argument("--variant-table-run", action="store_true",
+                    help="launch every step kernel a few times on one state (the run the "
+                         "counter table is profiled on) instead of the headline run")
+    ap.add_argument("--variant-table", metavar="DIR",
+                    help="no GPU run: print the per-variant counter table from the rocprofv3 "
+                         "passes under DIR (trace/, fetch/, write/, tcc/, occ/) over "
+                         "--variant-table-run")
     ap.add_argument("--traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="no GPU run: build the traffic record under profiles/ from "
                          "two rocprofv3 --pmc counter_collection.csv files of this bench")
@@ -277,6 +430,8 @@ def main():
     if args.traffic:
         write_traffic(*args.traffic, args.variant)
         return 0
+    if args.variant_table:
+        return variant_table(args.variant_table)
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py runs on one GPU only: the library has no multi-GPU path "
               "(the step would shard by z-slabs with a one-plane halo; not built). "
@@ -305,6 +460,8 @@ def main():
 
     if args.march_sweep:
         return march_sweep(args, tvf, torch, np, phantoms, dev, (nx, ny, nz), lam, n_inner)
+    if args.variant_table_run:
+        return variant_table_run(args, tvf, torch, phantoms, dev, (nx, ny, nz), lam, n_inner)
 
     t0 = time.time()
     b_host, p0_host, _ = phantoms.make_inputs(args.workload, (nx, ny, nz))
