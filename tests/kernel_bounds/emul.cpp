@@ -53,14 +53,16 @@ float *guarded(size_t bytes, bool end_aligned, unsigned seed) {
     perror("mprotect");
     exit(3);
   }
-  float *p = end_aligned ? (float *)(mid + span - bytes) : (float *)mid;
-  const size_t n = bytes / sizeof(float);
+  // A buffer of binary16 volumes may be only 2-byte aligned at its start, so
+  // the fill goes byte by byte (small floats, or binary16 halves of them).
+  char *p = end_aligned ? mid + span - bytes : mid;
   unsigned s = seed * 2654435761u + 1u;
-  for (size_t i = 0; i < n; ++i) {
+  for (size_t i = 0; i < bytes; i += sizeof(float)) {
     s = s * 1664525u + 1013904223u;
-    p[i] = ((float)(s >> 8) / 16777216.0f - 0.5f) * 0.1f;
+    const float v = ((float)(s >> 8) / 16777216.0f - 0.5f) * 0.1f;
+    memcpy(p + i, &v, bytes - i < sizeof(float) ? bytes - i : sizeof(float));
   }
-  return p;
+  return (float *)p;
 }
 
 template <typename F>
