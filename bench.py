@@ -2,15 +2,18 @@
 
 Prints one JSON line.  The metric is ms per FGP step over the whole volume;
 the default workload is the 512^3 ellipsoid phantom, 20 outer x 10 inner
-steps, lambda = 0.002, run by tv_fgp_run with the three-steps-per-pass kernel
-(variant tb3: three consecutive steps in one launch, bit for bit the same as
-three one-step launches; 200 steps = 66 launches of three and one of two).
+steps, lambda = 0.002, run by tv_fgp_run_pp with the three-steps-per-pass
+kernel (variant tb3: three consecutive steps in one launch, bit for bit the
+same as three one-step launches; 200 steps = 66 launches of three and one of
+two).  tv_fgp_run_pp is tv_fgp_run leaving p where the last pass wrote it (the
+caller's p or the workspace, reported like the r buffer) instead of copying
+it back.
 The timed region runs exactly --steps steps (in outer iterations of 10,
 momentum restarted at each) on one stream, bracketed by device
 synchronisation; inputs are resident in HBM before it starts.  It is run three
 times and `value` is the median (the page reports medians of repeated solves);
 `config.timed` lists the launches one timed region makes and whether p ends in
-the workspace and is copied back.
+the workspace.
 
 Besides the headline ms/step it reports:
   roofline      algorithmic bytes per launch (52 B per voxel: read b, r (3),
@@ -478,13 +481,21 @@ def main():
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
+    # the dual p and, for the multi-step variants, the workspace it alternates
+    # with: tv_fgp_run_pp leaves p where its last pass put it and says where
+    # (as it does for r), so pw[0] is always the current p
+    pw = [p, ws]
+
     def run(r_cur, r_nxt, n_outer, ni):
         if half and spl == 2:
             return tvf.tv_fgp_run2_h(b, p, ws, r_cur, r_nxt, lam, n_outer, ni, stream=stream)
         if half:
             return tvf.tv_fgp_run_h(b, p, r_cur, r_nxt, lam, n_outer, ni, stream=stream)
-        return tvf.tv_fgp_run(b, p, r_cur, r_nxt, lam, n_outer, ni, variant=variant, z_ws=ws,
-                              stream=stream)
+        r_where, p_where = tvf.tv_fgp_run_pp(b, pw[0], r_cur, r_nxt, lam, n_outer, ni,
+                                             variant=variant, z_ws=pw[1], stream=stream)
+        if p_where:
+            pw.reverse()
+        return r_where
 
     def step(r_cur, r_nxt, m):
         if half:
@@ -496,7 +507,8 @@ def main():
     def passes_of(k):
         """Launches tv_fgp_run makes for k steps in outer iterations of n_inner
         (passes of three and two steps, single steps) and whether p ends in
-        the workspace and is copied back."""
+        the workspace (tv_fgp_run would copy it back; tv_fgp_run_pp, which the
+        fp32 runs use, leaves it there)."""
         full, rest = divmod(k, n_inner)
         counts = {3: 0, 2: 0, 1: 0}
         copies = 0
@@ -560,6 +572,8 @@ def main():
         n_launch = max(1, args.steps // spl)
         evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(n_launch)]
+        if not half:
+            p, ws = pw
         p_cur, p_alt = p, ws
         for q in range(n_launch):
             k = q * spl
@@ -758,7 +772,8 @@ def main():
     timed = {"steps": args.steps,
              "launches": {"three_step": counts[3], "two_step": counts[2],
                           "one_step": counts[1]},
-             "p_copy_back": copies > 0,
+             "p_ends_in_workspace": copies > 0,
+             "p_copy_back": copies > 0 and half,
              "runs": 3}
     out = {
         "metric": METRIC if not half else METRIC.replace("fp32", "fp32 with binary16 p, r"),

@@ -179,6 +179,24 @@ int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
                void *stream, int *r_final);
 
 /*
+ * tv_fgp_run without the copy of p back from the workspace: with TV_FGP_TB2
+ * and TV_FGP_TB3, p alternates between the caller's p and z_ws from pass to
+ * pass, as r alternates between r_a and r_b, and the call reports where the
+ * last p is, as it reports r.  Same steps, same bits.
+ *   p_final   [out]  host pointer, required: 0 if the last p is in p, 1 if
+ *                    it is in z_ws (its three components at z_ws,
+ *                    z_ws + nx*ny*nz and z_ws + 2*nx*ny*nz); always 0 for the
+ *                    one-step variants, which update p in place.
+ * A run of an odd number of multi-step passes (20 steps with TB3: six passes
+ * of three and one of two) saves the copy of three volumes that tv_fgp_run
+ * makes.  Other arguments, errors and overlap rules as tv_fgp_run.
+ */
+int tv_fgp_run_pp(const float *b, float *const p[3], float *const r_a[3],
+                  float *const r_b[3], float lambda, int n_outer, int n_inner, int64_t nx,
+                  int64_t ny, int64_t nz, int variant, float *z_ws, void *stream,
+                  int *r_final, int *p_final);
+
+/*
  * Two consecutive FGP steps ("TV solver: the FGP step on the GPU", section
  * "What one step does", applied twice) in one pass over the volumes: the
  * first with momentum m1, the second with m2.  Reads b, p_in and r_in once,

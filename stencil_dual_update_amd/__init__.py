@@ -12,7 +12,7 @@ from ._lib import (  # noqa: F401
     TV_ERR_ALIAS, TV_ERR_ALIGN, TV_ERR_DIMS, TV_ERR_LAUNCH, TV_ERR_NULL,
     TV_ERR_PARAM, TV_ERR_VARIANT, TV_ERR_WORKSPACE, TV_OK, TvFgpError, lib,
     gap_workspace_bytes, momentum, status_string, tv_fgp_duality_gap,
-    tv_fgp_duality_gap_noalloc, tv_fgp_run,
+    tv_fgp_duality_gap_noalloc, tv_fgp_run, tv_fgp_run_pp,
     tv_fgp_run_h, tv_fgp_run2_h, tv_fgp_solve, tv_fgp_step, tv_fgp_step2, tv_fgp_step2_h,
     tv_fgp_step3, tv_fgp_step_h, tv_fgp_step_march, tv_fgp_stream_probe, tv_primal,
     tv_primal_h, MARCH_SHAPES,

@@ -36,7 +36,7 @@ VARIANTS = {"fused": FUSED, "lds_march": LDS_MARCH, "two_kernel": TWO_KERNEL,
             "cube_32x4x4": 11, "tb3": TB3}
 
 # Names declared in include/tv_fgp.h, in declaration order.
-EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_step_march", "tv_fgp_run", "tv_fgp_step2", "tv_fgp_step3",
+EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_step_march", "tv_fgp_run", "tv_fgp_run_pp", "tv_fgp_step2", "tv_fgp_step3",
            "tv_primal",
            "tv_fgp_step_h", "tv_fgp_run_h", "tv_fgp_step2_h", "tv_fgp_run2_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap",
            "tv_fgp_duality_gap_noalloc", "tv_fgp_solve",
@@ -80,6 +80,10 @@ def _load():
     lib.tv_fgp_run.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int,
                                I64, I64, I64, ctypes.c_int, P, P,
                                ctypes.POINTER(ctypes.c_int)]
+    lib.tv_fgp_run_pp.restype = ctypes.c_int
+    lib.tv_fgp_run_pp.argtypes = [P, P3, P3, P3, F, ctypes.c_int, ctypes.c_int,
+                                  I64, I64, I64, ctypes.c_int, P, P,
+                                  ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     lib.tv_fgp_step2.restype = ctypes.c_int
     lib.tv_fgp_step2.argtypes = [P, P3, P3, P3, P3, F, F, F, I64, I64, I64, P]
     lib.tv_fgp_step3.restype = ctypes.c_int
@@ -301,6 +305,24 @@ def tv_fgp_run(b, p, r_a, r_b, lam, n_outer, n_inner, variant=FUSED, z_ws=None,
                         _stream(stream), ctypes.byref(where))
     _raise(st, "tv_fgp_run")
     return where.value
+
+
+def tv_fgp_run_pp(b, p, r_a, r_b, lam, n_outer, n_inner, variant=FUSED, z_ws=None,
+                  stream=None, dims=None):
+    """tv_fgp_run without copying p back: returns (r_final, p_final), p_final 1
+    if the last p is in z_ws (its three volumes), 0 if in p."""
+    nx, ny, nz = _dims_of(b, dims)
+    shape = (nz, ny, nx)
+    _check_volume(b, shape, "b")
+    _check_ws(z_ws, shape, variant)
+    where = ctypes.c_int(-1)
+    pwhere = ctypes.c_int(-1)
+    st = lib.tv_fgp_run_pp(_addr(b), _field(p, shape, "p"), _field(r_a, shape, "r_a"),
+                           _field(r_b, shape, "r_b"), float(lam), int(n_outer),
+                           int(n_inner), nx, ny, nz, int(variant), _addr(z_ws),
+                           _stream(stream), ctypes.byref(where), ctypes.byref(pwhere))
+    _raise(st, "tv_fgp_run_pp")
+    return where.value, pwhere.value
 
 
 def tv_fgp_step2(b, p_in, p_out, r_in, r_out, lam, m1, m2, stream=None, dims=None):

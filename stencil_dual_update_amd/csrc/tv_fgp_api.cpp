@@ -104,12 +104,13 @@ int launch_status(int rc) { return rc == 0 ? TV_OK : TV_ERR_LAUNCH; }
 // pass may span two outer iterations and the result is the same as step by
 // step.  Threes end in twos rather than a single step where they can
 // (200 = 66 x 3 + 2, 10 = 3 + 3 + 2 + 2).  If p ends in the workspace it is
-// copied back.  `where` (0: r_a holds r, 1: r_b) flips after every launch.
-// The callables return 0 on success.
+// copied back, unless p_where is given: then *p_where is set to 1 (p is in
+// the workspace) or 0.  `where` (0: r_a holds r, 1: r_b) flips after every
+// launch.  The callables return 0 on success.
 template <typename T, typename Pass3, typename Pass2, typename Single>
 int enqueue_grouped(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], int n_outer,
                     int n_inner, size_t vol_bytes, void *stream, int *where, int max_group,
-                    Pass3 pass3, Pass2 pass2, Single single) {
+                    Pass3 pass3, Pass2 pass2, Single single, int *p_where = nullptr) {
   const size_t n = vol_bytes / sizeof(T);
   T *const ws[3] = {p_ws, p_ws + n, p_ws + 2 * n};
   T *const *cur = p;
@@ -148,6 +149,10 @@ int enqueue_grouped(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], in
     *where ^= 1;
     s += todo;
   }
+  if (p_where != nullptr) {
+    *p_where = cur != p ? 1 : 0;
+    return TV_OK;
+  }
   if (cur != p) {
     for (int q = 0; q < 3; ++q)
       if (hipMemcpyAsync(p[q], cur[q], vol_bytes, hipMemcpyDeviceToDevice,
@@ -161,18 +166,18 @@ int enqueue_grouped(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], in
 template <typename T, typename Pass, typename Single>
 int enqueue_pairs(T *const p[3], T *p_ws, T *const r_a[3], T *const r_b[3], int n_outer,
                   int n_inner, size_t vol_bytes, void *stream, int *where, Pass pass,
-                  Single single) {
+                  Single single, int *p_where = nullptr) {
   auto no_pass3 = [](T *const *, T *const *, T *const *, T *const *, float, float, float) {
     return (int)tvfgp::kLaunchFailed;
   };
   return enqueue_grouped<T>(p, p_ws, r_a, r_b, n_outer, n_inner, vol_bytes, stream, where, 2,
-                            no_pass3, pass, single);
+                            no_pass3, pass, single, p_where);
 }
 
 int enqueue_steps_tb2(const float *b, float *const p[3], float *const r_a[3],
                       float *const r_b[3], float lambda, float c, int n_outer,
                       int n_inner, int64_t nx, int64_t ny, int64_t nz,
-                      float *p_ws, size_t bytes, void *stream, int *where) {
+                      float *p_ws, size_t bytes, void *stream, int *where, int *p_where) {
   auto pass = [&](float *const *pi, float *const *po, float *const *ri, float *const *ro,
                   float m1, float m2) {
     tvfgp::Step2Args a;
@@ -199,13 +204,13 @@ int enqueue_steps_tb2(const float *b, float *const p[3], float *const r_a[3],
                                         tvfgp::kVariantFused, nullptr, stream));
   };
   return enqueue_pairs<float>(p, p_ws, r_a, r_b, n_outer, n_inner, bytes, stream, where, pass,
-                              single);
+                              single, p_where);
 }
 
 int enqueue_steps_tb3(const float *b, float *const p[3], float *const r_a[3],
                       float *const r_b[3], float lambda, float c, int n_outer,
                       int n_inner, int64_t nx, int64_t ny, int64_t nz,
-                      float *p_ws, size_t bytes, void *stream, int *where) {
+                      float *p_ws, size_t bytes, void *stream, int *where, int *p_where) {
   auto pass3 = [&](float *const *pi, float *const *po, float *const *ri, float *const *ro,
                    float m1, float m2, float m3) {
     tvfgp::Step3Args a;
@@ -253,21 +258,24 @@ int enqueue_steps_tb3(const float *b, float *const p[3], float *const r_a[3],
                                         tvfgp::kVariantFused, nullptr, stream));
   };
   return enqueue_grouped<float>(p, p_ws, r_a, r_b, n_outer, n_inner, bytes, stream, where, 3,
-                                pass3, pass2, single);
+                                pass3, pass2, single, p_where);
 }
 
 // Enqueue n_outer x n_inner steps; `where` (0: r_a holds r, 1: r_b) is
-// updated after every step, so the caller learns where the last r is.
+// updated after every step, so the caller learns where the last r is.  With
+// p_where given, the multi-step variants leave p where their last pass put
+// it and report it (1: the workspace) instead of copying it back.
 int enqueue_steps(const float *b, float *const p[3], float *const r_a[3],
                   float *const r_b[3], float lambda, float c, int n_outer,
                   int n_inner, int64_t nx, int64_t ny, int64_t nz, int variant,
-                  float *z_ws, void *stream, int *where) {
+                  float *z_ws, void *stream, int *where, int *p_where = nullptr) {
+  if (p_where != nullptr) *p_where = 0;
   if (variant == tvfgp::kVariantTb2)
     return enqueue_steps_tb2(b, p, r_a, r_b, lambda, c, n_outer, n_inner, nx, ny, nz, z_ws,
-                             volume_bytes(nx, ny, nz), stream, where);
+                             volume_bytes(nx, ny, nz), stream, where, p_where);
   if (variant == tvfgp::kVariantTb3)
     return enqueue_steps_tb3(b, p, r_a, r_b, lambda, c, n_outer, n_inner, nx, ny, nz, z_ws,
-                             volume_bytes(nx, ny, nz), stream, where);
+                             volume_bytes(nx, ny, nz), stream, where, p_where);
   for (int o = 0; o < n_outer; ++o) {
     double t = 1.0;
     for (int k = 1; k <= n_inner; ++k) {
@@ -410,6 +418,25 @@ int tv_fgp_run(const float *b, float *const p[3], float *const r_a[3],
   int where = 0;
   st = enqueue_steps(b, p, r_a, r_b, lambda, c, n_outer, n_inner, nx, ny, nz,
                      variant, z_ws, stream, &where);
+  if (r_final) *r_final = where;
+  return st;
+}
+
+int tv_fgp_run_pp(const float *b, float *const p[3], float *const r_a[3],
+                  float *const r_b[3], float lambda, int n_outer, int n_inner, int64_t nx,
+                  int64_t ny, int64_t nz, int variant, float *z_ws, void *stream,
+                  int *r_final, int *p_final) {
+  if (r_final) *r_final = 0;
+  if (p_final) *p_final = 0;
+  if (p_final == nullptr) return TV_ERR_NULL;
+  float c = 0.0f;
+  size_t bytes = 0;
+  int st = check_run(b, p, r_a, r_b, lambda, nx, ny, nz, variant, z_ws, &c, &bytes);
+  if (st != TV_OK) return st;
+  if (n_outer < 0 || n_inner < 0) return TV_ERR_PARAM;
+  int where = 0;
+  st = enqueue_steps(b, p, r_a, r_b, lambda, c, n_outer, n_inner, nx, ny, nz, variant, z_ws,
+                     stream, &where, p_final);
   if (r_final) *r_final = where;
   return st;
 }

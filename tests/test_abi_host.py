@@ -442,3 +442,38 @@ def probe(src=tuple(range(7)), dst=tuple(range(7, 13)), n=200):
 ])
 def test_stream_probe_rejects(kw, code):
     assert probe(**kw) == code
+
+
+def run_pp(b=0, p=(1, 2, 3), ra=(4, 5, 6), rb=(7, 8, 9), lam=0.01, n_outer=2, n_inner=3,
+           dims=(NX, NY, NZ), variant=0, ws=None, want_p=True):
+    where = ctypes.c_int(-7)
+    pwhere = ctypes.c_int(-7)
+    st = L.tv_fgp_run_pp(None if b is None else addr(b), field(*p), field(*ra), field(*rb),
+                         lam, n_outer, n_inner, *dims, variant,
+                         None if ws is None else addr(ws), None, ctypes.byref(where),
+                         ctypes.byref(pwhere) if want_p else None)
+    return st, where.value, pwhere.value
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(want_p=False), tvf.TV_ERR_NULL),         # p_final is required
+    (dict(b=None), tvf.TV_ERR_NULL),
+    (dict(n_outer=-1), tvf.TV_ERR_PARAM),
+    (dict(lam=float("inf")), tvf.TV_ERR_PARAM),
+    (dict(rb=(7, 8, 4)), tvf.TV_ERR_ALIAS),
+    (dict(variant=12), tvf.TV_ERR_WORKSPACE),      # three steps per pass without p workspace
+    (dict(variant=12, ws=9), tvf.TV_ERR_ALIAS),
+    (dict(variant=99), tvf.TV_ERR_VARIANT),
+])
+def test_run_pp_rejects(kw, code):
+    st, where, pwhere = run_pp(**kw)
+    assert st == code
+    assert where == 0
+    if kw.get("want_p", True):
+        assert pwhere == 0
+
+
+def test_run_pp_with_no_steps_enqueues_nothing():
+    for variant, ws in ((0, None), (12, 20)):
+        st, where, pwhere = run_pp(n_outer=0, n_inner=10, variant=variant, ws=ws)
+        assert (st, where, pwhere) == (tvf.TV_OK, 0, 0)

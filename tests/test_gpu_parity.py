@@ -282,6 +282,43 @@ def test_multistep_runs_span_outer_iterations(tvf, variant, no, ni):
     assert_bitwise(got, exp, "%s %dx%d" % (variant, no, ni))
 
 
+@pytest.mark.parametrize("variant", ["tb2", "tb3", "fused"])
+@pytest.mark.parametrize("no,ni", [(2, 10), (1, 7), (3, 4), (1, 3), (2, 1)], ids=lambda c: str(c))
+def test_run_pp_leaves_p_where_it_ends(tvf, variant, no, ni):
+    """tv_fgp_run_pp: p alternates with the workspace and is reported, not
+    copied back; the p it names equals the oracle bit for bit, and the other
+    buffer keeps the previous pass's p (multi-step variants) or stays
+    untouched (one-step variants)."""
+    b, p0, r0 = phantoms.make_inputs(4, (67, 21, 23))
+    exp = oracle_solve(b, p0, r0, 0.003, no, ni)
+    v = tvf.VARIANTS[variant]
+    dev = torch.device("cuda")
+    bt = torch.from_numpy(b).to(dev)
+    p = torch.from_numpy(p0).to(dev)
+    ra = torch.from_numpy(r0).to(dev)
+    rb = torch.full_like(ra, float("nan"))
+    ws = torch.full((3,) + tuple(bt.shape), float("nan"), device=dev)
+    rw, pw = tvf.tv_fgp_run_pp(bt, p, ra, rb, 0.003, no, ni, variant=v,
+                               z_ws=ws if v in (tvf.TB2, tvf.TB3) else None)
+    torch.cuda.synchronize()
+    if v not in (tvf.TB2, tvf.TB3):
+        assert pw == 0
+    pf = (ws if pw else p).cpu().numpy()
+    rf = (rb if rw else ra).cpu().numpy()
+    got = (pf, rf, oracle.primal(b, pf, 0.003))
+    assert_bitwise(got, exp, "run_pp %s %dx%d" % (variant, no, ni))
+    # the same run through tv_fgp_run ends with p in p: which buffer
+    # tv_fgp_run_pp names follows the number of multi-step passes
+    p2 = torch.from_numpy(p0).to(dev)
+    ra2 = torch.from_numpy(r0).to(dev)
+    rb2 = torch.empty_like(ra2)
+    ws2 = torch.empty_like(ws)
+    tvf.tv_fgp_run(bt, p2, ra2, rb2, 0.003, no, ni, variant=v,
+                   z_ws=ws2 if v in (tvf.TB2, tvf.TB3) else ws2[0] if v == tvf.TWO_KERNEL else None)
+    torch.cuda.synchronize()
+    assert np.array_equal(p2.cpu().numpy().view(np.uint32), pf.view(np.uint32))
+
+
 def test_no_steps_leaves_state(tvf):
     b, p0, r0 = phantoms.make_inputs(4, (40, 10, 6))
     for no, ni in ((0, 10), (3, 0)):
