@@ -244,7 +244,9 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
         own.pp0 = lds(pi0, own.o + j);
         own.pp1 = lds(pi1, own.o + j);
         own.pp2 = lds(pi2, own.o + j);
-        if (has_halo) {
+        // p is read at E1 points only: R0 points outside E1 feed the
+        // first primal alone
+        if (has_halo && hal.e1) {
           hal.pp0 = lds(pi0, hal.o + j);
           hal.pp1 = lds(pi1, hal.o + j);
           hal.pp2 = lds(pi2, hal.o + j);

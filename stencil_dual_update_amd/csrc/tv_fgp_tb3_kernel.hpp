@@ -202,7 +202,9 @@ __device__ __forceinline__ void tb3_tile(
       own.pp0 = lds(pi0, own.o + j);
       own.pp1 = lds(pi1, own.o + j);
       own.pp2 = lds(pi2, own.o + j);
-      if (has_halo) {
+      // p is read at E1 points only: R0 points outside E1 feed the first
+      // primal alone
+      if (has_halo && hx.e1) {
         hal.pp0 = lds(pi0, hal.o + j);
         hal.pp1 = lds(pi1, hal.o + j);
         hal.pp2 = lds(pi2, hal.o + j);
