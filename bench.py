@@ -792,8 +792,12 @@ def main():
              "p_ends_in_workspace": copies > 0,
              "p_copy_back": copies > 0 and half,
              "runs": 3}
+    # the headline metric's wording, with the volume actually run
+    metric = METRIC if not half else METRIC.replace("fp32", "fp32 with binary16 p, r")
+    if (nx, ny, nz) != (512, 512, 512):
+        metric = metric.replace("512³", "%d³" % nx if nx == ny == nz else "%d×%d×%d" % (nx, ny, nz))
     out = {
-        "metric": METRIC if not half else METRIC.replace("fp32", "fp32 with binary16 p, r"),
+        "metric": metric,
         "value": round(ms_per_step, 5),
         "unit": "ms/step",
         "n_gpus": 1,
