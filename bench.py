@@ -43,7 +43,9 @@ Besides the headline ms/step it reports:
                 roofline.pct_of_ceiling set the kernels against it.  It is
                 measured before the warm-up steps, after an untimed lead-in
                 of about 0.25 s (lead_in_launches) that also brings the GPU
-                from idle to its loaded clocks
+                from idle to its loaded clocks.  `shapes` holds the part's
+                rates for reading 7 volumes, writing 6 and copying one
+                (tv_fgp_stream_probe_ex)
   cpu_baseline  the CPU oracle (fp32, OpenMP over z planes) timed on the host
                 cores on a bounded sample: the first 10 outer iterations (100
                 steps) of the same workload at full size (with --storage half:
@@ -547,10 +549,11 @@ def main():
     # brings the GPU from idle to its loaded clocks before the warm-up steps;
     # without it the first timed region of a short run starts on a GPU that
     # is still ramping up.
-    ceil_ms, ceil_lead = None, 0
+    ceil_ms, ceil_lead, ceil_shapes = None, 0, {}
     if not args.no_copy and not half:
         vols = [torch.empty(nvox, dtype=torch.float32, device=dev).fill_(0.5)
                 for _ in range(13)]
+        torch.cuda.synchronize()  # the fills ran on the default stream
         with torch.cuda.stream(stream):
             t_lead = time.perf_counter()
             while ceil_lead < 3 or (time.perf_counter() - t_lead < 0.25 and ceil_lead < 2000):
@@ -566,7 +569,21 @@ def main():
                 tvf.tv_fgp_stream_probe(vols[:7], vols[7:], stream=stream)
             c1.record(stream)
             torch.cuda.synchronize()
-        ceil_ms = c0.elapsed_time(c1) / reps
+            ceil_ms = c0.elapsed_time(c1) / reps
+            # the part's rates for the read half, the write half and a copy
+            for name, ns, nd in (("read7", 7, 0), ("write6", 0, 6), ("copy1", 1, 1)):
+                srcs, dsts = vols[:ns], vols[7:7 + nd]
+                for _ in range(3):
+                    tvf.tv_fgp_stream_probe_ex(srcs, dsts, stream=stream)
+                c0.record(stream)
+                for _ in range(reps):
+                    tvf.tv_fgp_stream_probe_ex(srcs, dsts, stream=stream)
+                c1.record(stream)
+                torch.cuda.synchronize()
+                ms = c0.elapsed_time(c1) / reps
+                gbs = 4 * (ns + nd) * nvox / (ms * 1e-3) / 1e9
+                ceil_shapes[name] = {"ms": round(ms, 5), "gbps": round(gbs, 1),
+                                     "frac_of_hbm_peak": round(gbs / HBM_PEAK_GBS, 4)}
         del vols
 
     with torch.cuda.stream(stream):
@@ -724,7 +741,7 @@ def main():
         ceil_gbs = 52 * nvox / (ceil_ms * 1e-3) / 1e9
         ceiling = {"kernel": "stream13_kernel", "bytes": 52 * nvox, "ms": round(ceil_ms, 5),
                    "gbps": round(ceil_gbs, 1), "frac_of_hbm_peak": round(ceil_gbs / HBM_PEAK_GBS, 4),
-                   "lead_in_launches": ceil_lead}
+                   "lead_in_launches": ceil_lead, "shapes": ceil_shapes}
         if one_step is not None:
             one_step["pct_of_ceiling"] = round(100.0 * ceil_ms / one_step["ms_per_step"], 1)
         if args.variant in ("fused", "tb2", "tb3"):

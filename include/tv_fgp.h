@@ -386,8 +386,8 @@ float tv_fgp_momentum(int k);
  * the GPU" (section "Profiler counters" and its closing paragraph) prices a
  * fused step at 13 volumes, 7 read (b, p, r) and 6 written (p, r).  This call
  * writes dst[k][i] = src[k][i] + src[6][i] for k = 0..5 and i < n, reading
- * every src volume once (16-byte loads) and writing every dst volume once
- * (non-temporal 16-byte stores).
+ * every src volume once and writing every dst volume once, with
+ * non-temporal 16-byte loads and stores.
  *   src  [in]  7 device volumes of n floats, 16-byte aligned
  *   dst  [out] 6 device volumes of n floats, 16-byte aligned
  *   n    elements per volume, >= 1
@@ -397,6 +397,25 @@ float tv_fgp_momentum(int k);
  */
 int tv_fgp_stream_probe(const float *const src[7], float *const dst[6], int64_t n,
                         void *stream);
+
+/*
+ * Measurement helper, not a step: the part's streaming rates for the read and
+ * write halves of a step's traffic, beside the 13-volume mix above.  Shapes
+ * (n_src, n_dst) and what they write, for i < n:
+ *   (7, 6)  dst[k][i] = src[k][i] + src[6][i], k = 0..5 (tv_fgp_stream_probe)
+ *   (7, 0)  reads the seven volumes and writes nothing (their sum is dropped)
+ *   (0, 6)  dst[k][i] = k, k = 0..5
+ *   (1, 1)  dst[0][i] = src[0][i]
+ * Every volume is read or written once, with non-temporal 16-byte loads and
+ * stores.  src holds n_src device pointers (may be NULL when n_src = 0), dst
+ * holds n_dst (may be NULL when n_dst = 0); each volume is n floats, 16-byte
+ * aligned; no dst may overlap any other volume of the call.  Errors:
+ * TV_ERR_PARAM (another shape), TV_ERR_NULL, TV_ERR_DIMS (n < 1 or n*4
+ * overflows), TV_ERR_ALIGN, TV_ERR_ALIAS, TV_ERR_LAUNCH.  Enqueued on
+ * `stream`, no host synchronisation.
+ */
+int tv_fgp_stream_probe_ex(const float *const *src, int n_src, float *const *dst, int n_dst,
+                           int64_t n, void *stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char *tv_fgp_status_string(int status);

@@ -14,6 +14,7 @@ from ._lib import (  # noqa: F401
     gap_workspace_bytes, momentum, status_string, tv_fgp_duality_gap,
     tv_fgp_duality_gap_noalloc, tv_fgp_run, tv_fgp_run_pp,
     tv_fgp_run_h, tv_fgp_run2_h, tv_fgp_solve, tv_fgp_step, tv_fgp_step2, tv_fgp_step2_h,
-    tv_fgp_step3, tv_fgp_step_h, tv_fgp_step_march, tv_fgp_stream_probe, tv_primal,
+    tv_fgp_step3, tv_fgp_step_h, tv_fgp_step_march, tv_fgp_stream_probe,
+    tv_fgp_stream_probe_ex, STREAM_SHAPES, tv_primal,
     tv_primal_h, MARCH_SHAPES,
     variant_name, workspace_bytes)

@@ -41,7 +41,7 @@ EXPORTS = ("tv_fgp_step", "tv_fgp_step_ex", "tv_fgp_step_march", "tv_fgp_run", "
            "tv_fgp_step_h", "tv_fgp_run_h", "tv_fgp_step2_h", "tv_fgp_run2_h", "tv_primal_h", "tv_fgp_gap_workspace_bytes", "tv_fgp_duality_gap",
            "tv_fgp_duality_gap_noalloc", "tv_fgp_solve",
            "tv_fgp_workspace_bytes", "tv_fgp_momentum", "tv_fgp_stream_probe",
-           "tv_fgp_status_string", "tv_fgp_variant_name")
+           "tv_fgp_stream_probe_ex", "tv_fgp_status_string", "tv_fgp_variant_name")
 
 
 class TvFgpError(RuntimeError):
@@ -119,6 +119,8 @@ def _load():
     lib.tv_fgp_momentum.argtypes = [ctypes.c_int]
     lib.tv_fgp_stream_probe.restype = ctypes.c_int
     lib.tv_fgp_stream_probe.argtypes = [P3, P3, I64, P]
+    lib.tv_fgp_stream_probe_ex.restype = ctypes.c_int
+    lib.tv_fgp_stream_probe_ex.argtypes = [P, ctypes.c_int, P, ctypes.c_int, I64, P]
     lib.tv_fgp_status_string.restype = ctypes.c_char_p
     lib.tv_fgp_status_string.argtypes = [ctypes.c_int]
     lib.tv_fgp_variant_name.restype = ctypes.c_char_p
@@ -500,3 +502,28 @@ def tv_fgp_stream_probe(src, dst, stream=None):
     arr_d = (ctypes.c_void_p * 6)(*[t.data_ptr() for t in dst])
     st = lib.tv_fgp_stream_probe(arr_s, arr_d, n, _stream(stream))
     _raise(st, "tv_fgp_stream_probe")
+
+
+# Shapes of tv_fgp_stream_probe_ex: (sources, destinations)
+STREAM_SHAPES = ((7, 6), (7, 0), (0, 6), (1, 1))
+
+
+def tv_fgp_stream_probe_ex(src, dst, stream=None):
+    """The part's streaming rates for a step's read and write halves: with
+    (len(src), len(dst)) = (7, 6) dst[k] = src[k] + src[6]; (7, 0) the sources
+    are read and nothing is written; (0, 6) dst[k] = k; (1, 1) dst[0] = src[0].
+    All float32 device tensors, contiguous, with the same number of elements."""
+    src, dst = list(src), list(dst)
+    if (len(src), len(dst)) not in STREAM_SHAPES:
+        raise ValueError("tv_fgp_stream_probe_ex takes (sources, destinations) in %s"
+                         % (STREAM_SHAPES,))
+    n = (src or dst)[0].numel()
+    for t in src + dst:
+        _check_dev(t, "probe volume", "float32", n)
+        if t.numel() != n:
+            raise ValueError("probe volumes must have the same number of elements")
+    arr_s = (ctypes.c_void_p * max(1, len(src)))(*[t.data_ptr() for t in src])
+    arr_d = (ctypes.c_void_p * max(1, len(dst)))(*[t.data_ptr() for t in dst])
+    st = lib.tv_fgp_stream_probe_ex(arr_s if src else None, len(src), arr_d if dst else None,
+                                    len(dst), n, _stream(stream))
+    _raise(st, "tv_fgp_stream_probe_ex")

@@ -917,6 +917,21 @@ int tv_fgp_stream_probe(const float *const src[7], float *const dst[6], int64_t 
   return launch_status(tvfgp::launch_stream13(src, dst, n, stream));
 }
 
+int tv_fgp_stream_probe_ex(const float *const *src, int n_src, float *const *dst, int n_dst,
+                           int64_t n, void *stream) {
+  if (!tvfgp::stream_shape_supported(n_src, n_dst)) return TV_ERR_PARAM;
+  if ((n_src > 0 && src == nullptr) || (n_dst > 0 && dst == nullptr)) return TV_ERR_NULL;
+  const size_t bytes = volume_bytes(n, 1, 1);
+  if (bytes == 0) return TV_ERR_DIMS;
+  Buf bufs[13];
+  int count = 0;
+  for (int k = 0; k < n_src; ++k) bufs[count++] = Buf{src[k], bytes, 16, false};
+  for (int k = 0; k < n_dst; ++k) bufs[count++] = Buf{dst[k], bytes, 16, true};
+  const int st = check_buffers(bufs, count);
+  if (st != TV_OK) return st;
+  return launch_status(tvfgp::launch_stream(src, n_src, dst, n_dst, n, stream));
+}
+
 size_t tv_fgp_workspace_bytes(int variant, int64_t nx, int64_t ny, int64_t nz) {
   if (!known_variant(variant)) return 0;
   return run_workspace_bytes(variant, volume_bytes(nx, ny, nz));

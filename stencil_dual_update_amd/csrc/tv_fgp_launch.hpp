@@ -158,5 +158,8 @@ size_t gap_static_capacity_bytes();
 // elements (the 7-read / 6-write traffic of one step as a linear stream).
 // The volumes must be 16-byte aligned.
 int launch_stream13(const float *const src[7], float *const dst[6], int64_t n, void *stream);
+bool stream_shape_supported(int n_src, int n_dst);
+int launch_stream(const float *const *src, int n_src, float *const *dst, int n_dst, int64_t n,
+                  void *stream);
 
 }  // namespace tvfgp

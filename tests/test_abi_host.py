@@ -444,6 +444,36 @@ def test_stream_probe_rejects(kw, code):
     assert probe(**kw) == code
 
 
+def probe_ex(src=tuple(range(7)), n_src=7, dst=tuple(range(7, 13)), n_dst=6, n=200):
+    """tv_fgp_stream_probe_ex on fake volumes, as probe(); only calls that
+    fail validation are made."""
+    def arr(ks):
+        if ks is None:
+            return None
+        return (ctypes.c_void_p * max(1, len(ks)))(*[None if k is None else addr(k) if k < 1000
+                                                      else k for k in ks])
+    return L.tv_fgp_stream_probe_ex(arr(src), n_src, arr(dst), n_dst, n, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n_src=2, n_dst=2), tvf.TV_ERR_PARAM),
+    (dict(n_src=7, n_dst=5), tvf.TV_ERR_PARAM),
+    (dict(n_src=-1, n_dst=6), tvf.TV_ERR_PARAM),
+    (dict(src=None), tvf.TV_ERR_NULL),
+    (dict(dst=None), tvf.TV_ERR_NULL),
+    (dict(src=None, n_src=0, dst=None, n_dst=6), tvf.TV_ERR_NULL),
+    (dict(n_dst=0, dst=None, n=0), tvf.TV_ERR_DIMS),
+    (dict(n_src=1, n_dst=1, src=(0,), dst=(1,), n=-3), tvf.TV_ERR_DIMS),
+    (dict(n_src=1, n_dst=1, src=(addr(0) + 4,), dst=(1,)), tvf.TV_ERR_ALIGN),
+    (dict(n_src=0, src=None, dst=(7, 8, 9, 10, 11, addr(12) + 8)), tvf.TV_ERR_ALIGN),
+    (dict(n_src=1, n_dst=1, src=(0,), dst=(0,)), tvf.TV_ERR_ALIAS),
+    (dict(dst=(7, 8, 9, 10, 10, 12)), tvf.TV_ERR_ALIAS),
+    (dict(n_src=0, src=None, dst=(7, 8, 9, 10, 11, 7)), tvf.TV_ERR_ALIAS),
+])
+def test_stream_probe_ex_rejects(kw, code):
+    assert probe_ex(**kw) == code
+
+
 def run_pp(b=0, p=(1, 2, 3), ra=(4, 5, 6), rb=(7, 8, 9), lam=0.01, n_outer=2, n_inner=3,
            dims=(NX, NY, NZ), variant=0, ws=None, want_p=True):
     where = ctypes.c_int(-7)
