@@ -8,8 +8,8 @@
 // by two voxels in x and y, step two on the tile grown by one, step three on
 // the tile, keeping the intermediate p and r on chip: b, p and r are read
 // once and p, r written once per three steps.  On MI355X at 512^3 a launch
-// takes 1.88 ms, 0.63 ms per step (two steps per pass: 0.77; one: 1.30); its
-// HBM traffic is 1.26 x the compulsory bytes, moved at 4.7 TB/s, and it
+// takes 1.88 ms, 0.63 ms per step (two steps per pass: 0.76; one: 1.30); its
+// HBM traffic is 1.23 x the compulsory bytes, moved at 4.6 TB/s, and it
 // issues VALU instructions 70% of the time, so at two workgroups per CU the
 // pass is bound by instruction issue and latency together, not by memory
 // alone.  Most of the traffic above the compulsory bytes is the y-halo rows:
