@@ -11,7 +11,8 @@ it back.
 The timed region runs exactly --steps steps (in outer iterations of 10,
 momentum restarted at each) on one stream, bracketed by device
 synchronisation; inputs are resident in HBM before it starts.  It is run three
-times and `value` is the median (the page reports medians of repeated solves);
+times (five up to 256^3 voxels) and `value` is the median (the page reports
+medians of repeated solves);
 `config.timed` lists the launches one timed region makes and whether p ends in
 the workspace.
 
@@ -32,9 +33,10 @@ Besides the headline ms/step it reports:
                 p: 16 B per voxel) and the gap triple itself
   vs_one_step_roofline  the time a one-step pass needs at the 8 TB/s peak
                 (52 B per voxel per step) and its ratio to the measured ms/step
-  repeats       the timed region run twice more (ms/step of all three, their
-                median and spread) and T0, the same solve with zero dual steps
-                per outer iteration, with (T - T0) / steps
+  repeats       the timed region run again, 3 times in all above 256^3 voxels
+                and 5 times up to it (ms/step of every run, their median, which
+                is `value`, and spread) and T0, the same solve with zero dual
+                steps per outer iteration, with (T - T0) / steps
   copy          bandwidth of a plain device copy of 2 x 1 GiB on the same box
   ceiling       tv_fgp_stream_probe: the 7-read / 6-write traffic of one step
                 over the same volume size as a linear stream with
@@ -483,6 +485,9 @@ def main():
     ws = (torch.empty_like(b) if variant == tvf.TWO_KERNEL else
           torch.empty_like(p) if variant in (tvf.TB2, tvf.TB3) else None)
     spl = STEPS_PER_LAUNCH.get(args.variant, 1)
+    # timed regions: the median of 5 up to 256^3 voxels, of 3 above (the
+    # page's protocol: medians of repeated solves)
+    n_runs = 5 if nvox <= 256 ** 3 else 3
     stream = torch.cuda.Stream(device=dev)
     torch.cuda.synchronize()
 
@@ -602,7 +607,7 @@ def main():
         # the same timed region twice more (spread across runs), and the solve
         # with zero dual steps per outer iteration (T0: per step = (T - T0) / steps)
         repeat_ms = []
-        for _ in range(2):
+        for _ in range(n_runs - 1):
             start.record(stream)
             r_cur, r_nxt = run_steps(args.steps, r_cur, r_nxt)
             stop.record(stream)
@@ -644,15 +649,16 @@ def main():
         p = p_cur
         launch_ms = [e0.elapsed_time(e1) for e0, e1 in evs]
 
-    # the reported figure is the median of the three timed regions (the page
+    # the reported figure is the median of the timed regions (the page
     # reports medians of repeated solves)
     runs = sorted([region_ms] + repeat_ms)
-    ms_per_step = runs[1] / args.steps
+    mid = runs[len(runs) // 2]
+    ms_per_step = mid / args.steps
     repeats = {"ms_per_step": [round(v / args.steps, 5) for v in [region_ms] + repeat_ms],
                "median_ms_per_step": round(ms_per_step, 5),
-               "spread_pct": round(100.0 * (runs[-1] - runs[0]) / runs[1], 2),
+               "spread_pct": round(100.0 * (runs[-1] - runs[0]) / mid, 2),
                "t0_ms": round(t0_ms, 4),
-               "t_minus_t0_ms_per_step": round((runs[1] - t0_ms) / args.steps, 5)}
+               "t_minus_t0_ms_per_step": round((mid - t0_ms) / args.steps, 5)}
     step_bytes = (BYTES_PER_VOXEL_HALF if half else BYTES_PER_VOXEL[args.variant]) * nvox
     launch_avg_ms = float(np.mean(launch_ms))
     achieved = step_bytes / (launch_avg_ms * 1e-3) / 1e9
@@ -799,16 +805,17 @@ def main():
         base = "%s recipe at %dx%dx%d" % (base, nx, ny, nz)
     counts, copies = passes_of(args.steps)
     full, rest = divmod(args.steps, n_inner)
-    workload_label = "%s, lambda %g: %d steps timed (%s), median of 3 timed runs" % (
+    workload_label = "%s, lambda %g: %d steps timed (%s), median of %d timed runs" % (
         base, lam, args.steps,
         " + ".join(x for x in ("%d outer x %d inner" % (full, n_inner) if full else "",
-                               "1 outer x %d inner" % rest if rest else "") if x))
+                               "1 outer x %d inner" % rest if rest else "") if x),
+        n_runs)
     timed = {"steps": args.steps,
              "launches": {"three_step": counts[3], "two_step": counts[2],
                           "one_step": counts[1]},
              "p_ends_in_workspace": copies > 0,
              "p_copy_back": copies > 0 and half,
-             "runs": 3}
+             "runs": n_runs}
     # the headline metric's wording, with the volume actually run
     metric = METRIC if not half else METRIC.replace("fp32", "fp32 with binary16 p, r")
     if (nx, ny, nz) != (512, 512, 512):
