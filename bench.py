@@ -251,6 +251,96 @@ def march_sweep(args, tvf, torch, np, phantoms, dev, dims, lam, n_inner):
     return 0
 
 
+# Cube edge lengths of the size sweep (the ellipsoid recipe at each size).
+SIZE_SWEEP = (64, 96, 128, 192, 256, 320, 384, 448, 512, 640, 768)
+
+
+def size_sweep(args, tvf, torch, phantoms, dev, lam, n_inner):
+    """ms per step against volume size.  At each size, after the inputs are
+    made on the host: the 7-read / 6-write stream (tv_fgp_stream_probe) for
+    an untimed quarter of a second (which also brings the GPU back to its
+    loaded clocks), then timed (the median of 20 launches); the three-step
+    run (tv_fgp_run_pp, 30 steps after 6 warm-up steps, the median of 3
+    runs); the one-step kernel (tv_fgp_step, the median of 20 launches after
+    5)."""
+    rows = []
+    stream = torch.cuda.Stream(device=dev)
+
+    def med(ts):
+        ts = sorted(ts)
+        return ts[len(ts) // 2]
+
+    def launch_times(fn, count, skip):
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(count + skip)]
+        for q, (a, z) in enumerate(evs):
+            a.record(stream)
+            fn(q)
+            z.record(stream)
+        torch.cuda.synchronize()
+        return [a.elapsed_time(z) for a, z in evs[skip:]]
+
+    for n in SIZE_SWEEP:
+        dims = (n, n, n)
+        nvox = n ** 3
+        b_host, p0_host, _ = phantoms.make_inputs(3, dims)
+        vols = [torch.empty(nvox, dtype=torch.float32, device=dev).fill_(0.5) for _ in range(13)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            t_lead = time.perf_counter()
+            while time.perf_counter() - t_lead < 0.25:
+                for _ in range(3):
+                    tvf.tv_fgp_stream_probe(vols[:7], vols[7:], stream=stream)
+                torch.cuda.synchronize()
+            tc = launch_times(lambda q: tvf.tv_fgp_stream_probe(vols[:7], vols[7:], stream=stream),
+                              20, 0)
+        del vols
+        b = torch.from_numpy(b_host).to(dev)
+        p = torch.from_numpy(p0_host).to(dev)
+        ws = torch.empty_like(p)
+        rr = [p.clone(), torch.empty_like(p)]
+        pw = [p, ws]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            def run(n_outer, ni):
+                r_where, p_where = tvf.tv_fgp_run_pp(b, pw[0], rr[0], rr[1], lam, n_outer, ni,
+                                                     variant=tvf.TB3, z_ws=pw[1], stream=stream)
+                if p_where:
+                    pw.reverse()
+                if r_where:
+                    rr.reverse()
+            run(1, 6)
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            t3 = []
+            for _ in range(3):
+                e0.record(stream)
+                run(3, n_inner)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t3.append(e0.elapsed_time(e1) / (3 * n_inner))
+
+            def one(q):
+                tvf.tv_fgp_step(b, pw[0], rr[0], rr[1], lam, tvf.momentum(q % n_inner + 1),
+                                stream=stream)
+                rr.reverse()
+            t1 = launch_times(one, 20, 5)
+        del b, p, ws, rr, pw
+        m3, m1, mc = med(t3), med(t1), med(tc)
+        row = {"n": n, "voxels": nvox, "working_set_mb": round(13 * 4 * nvox / 2 ** 20, 1),
+               "three_step_ms_per_step": round(m3, 5), "one_step_ms": round(m1, 5),
+               "stream_ms": round(mc, 5),
+               "three_step_step_gbps": round(52 * nvox / (m3 * 1e-3) / 1e9, 1),
+               "one_step_gbps": round(52 * nvox / (m1 * 1e-3) / 1e9, 1),
+               "stream_gbps": round(52 * nvox / (mc * 1e-3) / 1e9, 1),
+               "one_step_pct_of_stream": round(100 * mc / m1, 1),
+               "three_step_speedup": round(m1 / m3, 2)}
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    print(json.dumps({"size_sweep": rows, "device": torch.cuda.get_device_name(dev)}), flush=True)
+    return 0
+
+
 # Variants of the counter table and the kernels each launches (name prefixes
 # as the kernel trace prints them).
 TABLE_VARIANTS = [("fused", ["fused_zx_kernel"]), ("pair", ["fused_pair_kernel"]),
@@ -415,6 +505,9 @@ def parse():
     ap.add_argument("--storage", default="f32", choices=["f32", "half"],
                     help="storage of the dual p and r (half: binary16, fused kernel only)")
     ap.add_argument("--no-copy", action="store_true", help="skip the copy probe")
+    ap.add_argument("--size-sweep", action="store_true",
+                    help="ms per step of the three-step run, the one-step kernel and the "
+                         "13-volume stream at cube sizes 64^3 .. 768^3 (ellipsoid recipe)")
     ap.add_argument("--march-sweep", action="store_true",
                     help="time the LDS z-march kernel at every tile shape of the page's sweep "
                          "(one step per launch) instead of the headline run")
@@ -470,6 +563,8 @@ def main():
 
     if args.march_sweep:
         return march_sweep(args, tvf, torch, np, phantoms, dev, (nx, ny, nz), lam, n_inner)
+    if args.size_sweep:
+        return size_sweep(args, tvf, torch, phantoms, dev, lam, n_inner)
     if args.variant_table_run:
         return variant_table_run(args, tvf, torch, phantoms, dev, (nx, ny, nz), lam, n_inner)
 
