@@ -119,10 +119,13 @@ def test_lds_one_step(func, tmp_path, kernel, dims):
                                            ("lds_march_32x8", 8), ("lds_march_32x16", 16),
                                            ("lds_march_64x8", 8), ("lds_march", 16)],
                          ids=lambda c: str(c))
-@pytest.mark.parametrize("dims", [(37, 19, 11), (70, 33, 40), (1, 1, 1)], ids=lambda d: str(d))
+@pytest.mark.parametrize("dims", [(37, 19, 11), (70, 33, None), (1, 1, 1)], ids=lambda d: str(d))
 def test_lds_march_shapes_one_step(func, tmp_path, kernel, planes, dims):
     """The marching kernel at the tile shapes of the page's sweep, one step
-    against the oracle bit for bit (tiles and plane slabs ragged at the faces)."""
+    against the oracle bit for bit (tiles and plane slabs ragged at the faces;
+    nz None: one full slab of the shape's planes and a ragged one of 3)."""
+    if dims[2] is None:
+        dims = (dims[0], dims[1], planes + 3)
     b, p0, r0 = inputs(dims)
     pg, rg = emulate(func, tmp_path, kernel, b, p0, r0, 0.003, np.float32(0.4), 0.0,
                      planes=planes)
