@@ -417,12 +417,12 @@ def test_workload3_512_full_200_steps_all_variants(tvf):
 def test_workload4_anisotropic_full_200_steps(tvf):
     """1000 x 777 x 301 (rows of 1000 floats, not a multiple of a cache line;
     ragged tiles on every face): the whole volume after the full 20 x 10 steps,
-    from a random admissible p with r = p, for the one-step kernel and the two-
-    and three-steps-per-pass runs (the latter: 66 three-step passes, one
-    two-step pass and the copy of p back from the workspace)."""
+    from a random admissible p with r = p, for every variant (the three-steps-
+    per-pass run: 66 three-step passes, one two-step pass and the copy of p
+    back from the workspace)."""
     b, p0, r0, lam, no, ni, exp = reference(4)
     assert b.shape == (301, 777, 1000)
-    for variant in ("fused", "tb2", "tb3"):
+    for variant in VARIANTS:
         print("1000x777x301 %s: %d x %d steps" % (variant, no, ni), flush=True)
         got = gpu_solve(tvf, b, p0, r0, lam, no, ni, variant)
         assert_close(got, exp, "1000x777x301 " + variant)
