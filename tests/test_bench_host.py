@@ -22,6 +22,15 @@ def test_more_than_one_gpu_is_refused():
     assert r.stdout == ""
 
 
+def test_help_lists_the_modes():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--help"],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0
+    for flag in ("--steps", "--warmup", "--gpus", "--variant", "--storage", "--workload",
+                 "--dims", "--size-sweep", "--march-sweep", "--variant-table", "--traffic"):
+        assert flag in r.stdout, flag
+
+
 def test_strip_comments_ignores_comments_and_layout_only():
     src = 'int a = 1; // one\n/* block\n comment */ float s = "x // y"; char c = \'/\';\n'
     assert bench.strip_comments(src) == 'int a = 1; float s = "x // y"; char c = \'/\';'
