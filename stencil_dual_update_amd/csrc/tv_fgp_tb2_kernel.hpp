@@ -28,7 +28,8 @@
 // Iteration k of the z march (k runs from z0 - 4 to z1 - 1 for the slab
 // [z0, z1); the first iterations only fill the pipeline):
 //   phase 1: z1 at plane k+1 on R1 (from r' of planes k+1 and k);
-//            z0 at plane k+3 on R0 (from the loads of plane k+3)
+//            z0 at plane k+3 on R0 (from the loads of plane k+3); then
+//            the loads of plane k+4 go into the registers plane k+3 came in
 //   barrier
 //   phase 2: step two at plane k on the tile -> p_out, r_out;
 //            step one at plane k+2 on E1 -> r' into LDS, own p', r' kept
@@ -84,8 +85,8 @@ struct TbPoint {
   bool e1, r1, own;         // member of E1, R1, the tile
   bool low_x, low_y, has_x, has_y;
   Off o;                    // byte offset of the column at plane 0
-  float cb, c0, c1, c2, c0l, c1l;  // inputs of plane k+3
-  float nb, n0, n1, n2, n0l, n1l;  // inputs of plane k+4 (loads in flight)
+  float cb, c0, c1, c2, c0l, c1l;  // inputs of the first primal's next plane
+  float nb, n0, n1, n2, n0l, n1l;  // binary16 pipeline: the plane after it
   float q0, q1, q2;                // r of plane k+2
   float bq, bqq;                   // b of planes k+2 and k+1
   float pp0, pp1, pp2;             // p_in of plane k+2
@@ -115,7 +116,17 @@ __device__ __forceinline__ void tb_init_point(TbPoint<Off> &pt, int lx, int ly, 
   pt.pp0 = pt.pp1 = pt.pp2 = 0.0f;
 }
 
-// Loads of plane kp into the "next" registers (caller checks 0 <= kp < nz).
+// A value as it reads back after a store to an S volume (identity for float;
+// for _Float16 the round to nearest, ties to even, widened again exactly).
+template <typename S>
+__device__ __forceinline__ float as_stored(float v) {
+  return (float)(S)v;
+}
+
+// Loads of plane kp into the input registers of a point (caller checks
+// 0 <= kp < nz).  The z march issues them once the first primal has used the
+// previous plane's values, so they stay in flight across the barrier and the
+// next plane's other work, and no register with a load in flight is copied.
 // A point outside the volume has offset 0 and loads the plane's first voxel,
 // which is in bounds; its values are never used.  S is the element type of
 // the dual volumes (float, or _Float16: widened exactly).
@@ -127,29 +138,33 @@ __device__ __forceinline__ void tb_load(TbPoint<Off> &pt, Off kp_off, Off sy4,
                                         const S *__restrict__ r2) {
   const Off four = 4;
   const Off j = pt.o + kp_off;
+  pt.cb = ld(b, j);
+  pt.c0 = lds(r0, j);
+  pt.c1 = lds(r1, j);
+  pt.c2 = lds(r2, j);
+  pt.c0l = lds(r0, pt.low_x ? j - four : j);
+  pt.c1l = lds(r1, pt.low_y ? j - sy4 : j);
+}
+
+// The same loads into the "n" registers, and the rotation that makes them
+// current at the end of a plane: the two-step kernel's binary16 pipeline,
+// which issues the next plane's loads at the top of the plane (measured 7%
+// faster there than loading after the first primal, which the fp32
+// instantiations do).
+template <typename S, typename Off>
+__device__ __forceinline__ void tb_load_next(TbPoint<Off> &pt, Off kp_off, Off sy4,
+                                             const float *__restrict__ b,
+                                             const S *__restrict__ r0,
+                                             const S *__restrict__ r1,
+                                             const S *__restrict__ r2) {
+  const Off four = 4;
+  const Off j = pt.o + kp_off;
   pt.nb = ld(b, j);
   pt.n0 = lds(r0, j);
   pt.n1 = lds(r1, j);
   pt.n2 = lds(r2, j);
   pt.n0l = lds(r0, pt.low_x ? j - four : j);
   pt.n1l = lds(r1, pt.low_y ? j - sy4 : j);
-}
-
-// A value as it reads back after a store to an S volume (identity for float;
-// for _Float16 the round to nearest, ties to even, widened again exactly).
-template <typename S>
-__device__ __forceinline__ float as_stored(float v) {
-  return (float)(S)v;
-}
-
-template <typename Off>
-__device__ __forceinline__ void tb_take(TbPoint<Off> &pt) {
-  pt.cb = pt.nb;
-  pt.c0 = pt.n0;
-  pt.c1 = pt.n1;
-  pt.c2 = pt.n2;
-  pt.c0l = pt.n0l;
-  pt.c1l = pt.n1l;
 }
 
 template <typename Off>
@@ -168,8 +183,8 @@ __device__ __forceinline__ void tb_rotate(TbPoint<Off> &pt) {
 }
 
 // Six waves per SIMD (three workgroups per CU) measured ~9% faster than the
-// five the unconstrained register allocation allows; the cap costs a couple
-// of spilled registers.
+// five the unconstrained register allocation allows; the 32-bit-offset
+// instantiations fit the cap (74 VGPRs) without spilling.
 // S: element type of p and r (float, or _Float16 for the binary16 dual, where
 // the first step's p' and r' are rounded to binary16 as a stored step's are).
 template <typename I, typename Off, typename S>
@@ -227,8 +242,13 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
       tb_load<S, Off>(own, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
       if (has_halo) tb_load<S, Off>(hal, (Off)(z0 - 1) * sz4, sy4, b, ri0, ri1, ri2);
     }
-    tb_take(own);
-    tb_take(hal);
+    // fp32: the next plane's loads go into the registers of the plane the
+    // first primal has just used, whose b and r are kept here for step one
+    // in the next iteration; binary16: they go into the "n" registers at the
+    // top of the plane and rotate in at its end
+    constexpr bool kLateLoads = sizeof(S) == 4;
+    float ot_b = 0.0f, ot_0 = 0.0f, ot_1 = 0.0f, ot_2 = 0.0f;
+    float ht_b = 0.0f, ht_0 = 0.0f, ht_1 = 0.0f, ht_2 = 0.0f;
 
     for (I k = kstart; k < z1; ++k) {
       const I kd = k + 2;  // step-one plane
@@ -252,11 +272,10 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
           hal.pp2 = lds(pi2, hal.o + j);
         }
       }
-      // inputs of plane k+4, consumed next iteration
       const I kl = k + 4;
-      if (input_plane(kl)) {
-        tb_load<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
-        if (has_halo) tb_load<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+      if (!kLateLoads && input_plane(kl)) {
+        tb_load_next<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+        if (has_halo) tb_load_next<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
       }
 
       // ---- phase 1: z1 of plane k+1 on R1, z0 of plane k+3 on R0
@@ -284,6 +303,22 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
       if (do_b) {
         if (own.ok) phase_b(own);
         if (hal.ok) phase_b(hal);
+      }
+      if (kLateLoads) {
+        // plane k+3 has been used; its b and r move aside and the loads of
+        // plane k+4 take its registers
+        ot_b = own.cb;
+        ot_0 = own.c0;
+        ot_1 = own.c1;
+        ot_2 = own.c2;
+        ht_b = hal.cb;
+        ht_0 = hal.c0;
+        ht_1 = hal.c1;
+        ht_2 = hal.c2;
+        if (input_plane(kl)) {
+          tb_load<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+          if (has_halo) tb_load<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+        }
       }
       __syncthreads();
 
@@ -341,8 +376,22 @@ __global__ __launch_bounds__(kTbBlock, 6) void tb2_kernel(
         }
       }
       __syncthreads();
-      tb_rotate(own);
-      tb_rotate(hal);
+      if (kLateLoads) {
+        // b and r of plane k+3 become those of plane k+2 for the next step
+        own.bqq = own.bq;
+        own.bq = ot_b;
+        own.q0 = ot_0;
+        own.q1 = ot_1;
+        own.q2 = ot_2;
+        hal.bqq = hal.bq;
+        hal.bq = ht_b;
+        hal.q0 = ht_0;
+        hal.q1 = ht_1;
+        hal.q2 = ht_2;
+      } else {
+        tb_rotate(own);
+        tb_rotate(hal);
+      }
     }
   }
 }

@@ -8,9 +8,9 @@
 // by two voxels in x and y, step two on the tile grown by one, step three on
 // the tile, keeping the intermediate p and r on chip: b, p and r are read
 // once and p, r written once per three steps.  On MI355X at 512^3 a launch
-// takes 1.88 ms, 0.63 ms per step (two steps per pass: 0.76; one: 1.30); its
-// HBM traffic is 1.23 x the compulsory bytes, moved at 4.6 TB/s, and it
-// issues VALU instructions 70% of the time, so at two workgroups per CU the
+// takes 1.85 ms, 0.62 ms per step (two steps per pass: 0.75; one: 1.30); its
+// HBM traffic is 1.21 x the compulsory bytes, moved at 4.5 TB/s, and it
+// issues VALU instructions 65% of the time, so at two workgroups per CU the
 // pass is bound by instruction issue and latency together, not by memory
 // alone.  Most of the traffic above the compulsory bytes is the y-halo rows:
 // the tiles above and below run on the same XCD but drift apart by more
@@ -33,7 +33,10 @@
 //
 // Iteration k of the z march (k from z0 - 7 to z1 - 1 for the slab [z0, z1)):
 //   phase 1: z2 at plane k+1 on R2, z1 at plane k+3 on R1, z0 at plane k+5
-//            on R0 (from the loads of plane k+5)
+//            on R0 (from the loads of plane k+5); then the loads of plane
+//            k+6 go into the registers plane k+5 came in, so they are in
+//            flight through phase 2 and the next phase 1 and no register
+//            with a load in flight is ever copied
 //   barrier
 //   phase 2: step three at plane k on T -> p_out, r_out;
 //            step two at plane k+2 on E2 -> r2 into LDS, p2 and r2 kept;
@@ -181,8 +184,9 @@ __device__ __forceinline__ void tb3_tile(
     tb_load<S, Off>(own, (Off)(z0 - 2) * sz4, sy4, b, ri0, ri1, ri2);
     if (has_halo) tb_load<S, Off>(hal, (Off)(z0 - 2) * sz4, sy4, b, ri0, ri1, ri2);
   }
-  tb_take(own);
-  tb_take(hal);
+  // b and r of plane k+5, kept after the loads of plane k+6 replace them
+  float ot_b = 0.0f, ot_0 = 0.0f, ot_1 = 0.0f, ot_2 = 0.0f;
+  float ht_b = 0.0f, ht_0 = 0.0f, ht_1 = 0.0f, ht_2 = 0.0f;
 
   for (I k = kstart; k < z1; ++k) {
     const I kd1 = k + 4;  // step-one plane
@@ -210,12 +214,7 @@ __device__ __forceinline__ void tb3_tile(
         hal.pp2 = lds(pi2, hal.o + j);
       }
     }
-    // inputs of plane k+6, consumed next iteration
     const I kl = k + 6;
-    if (input_plane(kl)) {
-      tb_load<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
-      if (has_halo) tb_load<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
-    }
 
     // ---- phase 1: z2 of plane k+1 on R2, z1 of plane k+3 on R1, z0 of
     // plane k+5 on R0.  Every index is inside its array (the lower
@@ -254,6 +253,20 @@ __device__ __forceinline__ void tb3_tile(
     if (do_b) {
       if (own.ok) phase_b(own);
       if (hal.ok) phase_b(hal);
+    }
+    // plane k+5's b and r are still needed (step one next iteration); the
+    // registers take the loads of plane k+6
+    ot_b = own.cb;
+    ot_0 = own.c0;
+    ot_1 = own.c1;
+    ot_2 = own.c2;
+    ht_b = hal.cb;
+    ht_0 = hal.c0;
+    ht_1 = hal.c1;
+    ht_2 = hal.c2;
+    if (input_plane(kl)) {
+      tb_load<S, Off>(own, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
+      if (has_halo) tb_load<S, Off>(hal, (Off)kl * sz4, sy4, b, ri0, ri1, ri2);
     }
     __syncthreads();
 
@@ -334,8 +347,18 @@ __device__ __forceinline__ void tb3_tile(
     ox.b2 = own.bqq;
     hx.b1 = hx.b2;
     hx.b2 = hal.bqq;
-    tb_rotate(own);
-    tb_rotate(hal);
+    // b and r of plane k+5 move down a plane; the loads of plane k+6 are
+    // already in place, so no register with a load in flight is copied
+    own.bqq = own.bq;
+    own.bq = ot_b;
+    own.q0 = ot_0;
+    own.q1 = ot_1;
+    own.q2 = ot_2;
+    hal.bqq = hal.bq;
+    hal.bq = ht_b;
+    hal.q0 = ht_0;
+    hal.q1 = ht_1;
+    hal.q2 = ht_2;
   }
 }
 
