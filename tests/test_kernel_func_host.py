@@ -194,12 +194,15 @@ def test_two_steps_per_pass_binary16(func, tmp_path, dims, planes):
 # (dims, 64-bit path, forced grid, slab length; 0 = as launched) for the
 # three-steps-per-pass kernel: slab ends, ragged tails, nz below a slab, one
 # voxel, tiles looped over by a short grid, each slab length the launcher picks
-# (dims, wide, grid, planes); (140, 27, 20) and (200, 20, 12) hold tiles
-# whose whole halo lies inside the volume (the kernel's interior path)
+# (dims, wide, grid, planes); the shapes from (140, 27, 20) on hold tiles
+# whose whole halo lies inside the volume (the kernel's interior path, whose
+# loads are unconditional and clamp their planes): fewer planes than the
+# pipeline's depth, a long slab, several slabs over a short grid
 CASES3 = [((65, 9, 17), 0, 0, 0), ((64, 8, 48), 1, 0, 16), ((130, 17, 33), 0, 3, 0),
           ((1, 1, 40), 0, 0, 32), ((5, 70, 3), 0, 0, 0), ((63, 7, 15), 0, 0, 8), ((1, 1, 1), 0, 0, 0),
           ((66, 10, 18), 1, 2, 16), ((64, 8, 200), 0, 0, 96), ((70, 13, 9), 0, 0, 8),
-          ((140, 27, 20), 0, 0, 8), ((200, 20, 12), 1, 3, 8)]
+          ((140, 27, 20), 0, 0, 8), ((200, 20, 12), 1, 3, 8), ((140, 20, 3), 0, 0, 0),
+          ((140, 20, 110), 0, 0, 96), ((200, 28, 40), 0, 5, 16)]
 
 
 def emulate3(func, tmp_path, kernel, b, p0, r0, lam, m, wide=0, grid=0, planes=0):
@@ -229,7 +232,8 @@ def test_three_steps_per_pass(func, tmp_path, dims, wide, grid, planes):
     assert_bits(rg, re, "r %s" % (dims,))
 
 
-@pytest.mark.parametrize("dims,planes", [((65, 9, 17), 0), ((64, 8, 48), 16), ((5, 70, 3), 0)],
+@pytest.mark.parametrize("dims,planes", [((65, 9, 17), 0), ((64, 8, 48), 16), ((5, 70, 3), 0),
+                                         ((140, 20, 12), 8)],
                          ids=lambda c: str(c))
 def test_three_steps_per_pass_binary16(func, tmp_path, dims, planes):
     """The binary16 instantiation equals three steps of the oracle's half mode."""
