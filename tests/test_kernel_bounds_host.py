@@ -28,10 +28,10 @@ VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "p
             "lds_march_32x16", "lds_march_64x8", "primal",
             "primal_h", "gap", "gap_pair", "tb2", "tb2_h", "tb3", "tb3_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8",
             "cube_32x4x4"]
-# shapes with tiles whose whole three-step halo lies inside the volume (the
-# three-step kernel's interior path, which clamps the planes it loads), from
-# fewer planes than the pipeline's depth to several slabs
-TB3_INTERIOR_SHAPES = [(140, 27, 20), (200, 20, 3), (140, 20, 1), (260, 28, 40), (200, 36, 9),
+# shapes with tiles whose whole two- or three-step halo lies inside the
+# volume (the multi-step kernels' interior path), from fewer planes than the
+# pipeline's depth to several slabs
+INTERIOR_SHAPES = [(140, 27, 20), (200, 20, 3), (140, 20, 1), (260, 28, 40), (200, 36, 9),
                        (140, 20, 100)]
 FOUR_PLANE = ("tb2", "tb2_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8", "cube_32x4x4", "fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
               "pair_h", "pair_nostream_h", "point", "gap", "gap_pair")
@@ -56,7 +56,7 @@ def emul(tmp_path_factory):
 @pytest.mark.parametrize("variant", VARIANTS)
 def test_every_access_in_bounds(emul, variant):
     failures = []
-    shapes = SHAPES + (TB3_INTERIOR_SHAPES if variant.startswith("tb3") else [])
+    shapes = SHAPES + (INTERIOR_SHAPES if variant.startswith(("tb2", "tb3")) else [])
     for nx, ny, nz in shapes:
         for wide in (0, 1):
             for end in (0, 1):

@@ -163,7 +163,10 @@ def test_duality_gap(func, tmp_path, kernel, dims, grid):
 # grid, each slab length the launcher picks
 CASES = [((65, 9, 17), 0, 0, 0), ((64, 8, 48), 1, 0, 16), ((130, 17, 33), 0, 3, 0),
          ((1, 1, 40), 0, 0, 32), ((5, 70, 3), 0, 0, 0), ((63, 7, 15), 0, 0, 0), ((1, 1, 1), 0, 0, 0),
-         ((66, 10, 18), 1, 2, 16), ((64, 8, 70), 0, 0, 32)]
+         ((66, 10, 18), 1, 2, 16), ((64, 8, 70), 0, 0, 32),
+         # tiles whose whole halo lies inside the volume (the kernel's interior
+         # path): several slabs, a short grid, the 64-bit path, a shallow z
+         ((140, 27, 20), 0, 0, 8), ((200, 28, 40), 1, 5, 16), ((140, 20, 2), 0, 0, 0)]
 
 
 @pytest.mark.parametrize("dims,wide,grid,planes", CASES, ids=lambda c: str(c))
@@ -177,7 +180,8 @@ def test_two_steps_per_pass(func, tmp_path, dims, wide, grid, planes):
     assert_bits(rg, re, "r %s" % (dims,))
 
 
-@pytest.mark.parametrize("dims,planes", [((65, 9, 17), 0), ((64, 8, 48), 16), ((5, 70, 3), 0)],
+@pytest.mark.parametrize("dims,planes", [((65, 9, 17), 0), ((64, 8, 48), 16), ((5, 70, 3), 0),
+                                         ((140, 20, 12), 8)],
                          ids=lambda c: str(c))
 def test_two_steps_per_pass_binary16(func, tmp_path, dims, planes):
     """The binary16 two-step pass equals two steps of the oracle's half mode."""
