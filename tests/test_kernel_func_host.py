@@ -164,8 +164,8 @@ def test_duality_gap(func, tmp_path, kernel, dims, grid):
 CASES = [((65, 9, 17), 0, 0, 0), ((64, 8, 48), 1, 0, 16), ((130, 17, 33), 0, 3, 0),
          ((1, 1, 40), 0, 0, 32), ((5, 70, 3), 0, 0, 0), ((63, 7, 15), 0, 0, 0), ((1, 1, 1), 0, 0, 0),
          ((66, 10, 18), 1, 2, 16), ((64, 8, 70), 0, 0, 32),
-         # tiles whose whole halo lies inside the volume (the kernel's interior
-         # path): several slabs, a short grid, the 64-bit path, a shallow z
+         # tiles whose whole halo lies inside the volume: several slabs, a
+         # short grid, the 64-bit path, a shallow z
          ((140, 27, 20), 0, 0, 8), ((200, 28, 40), 1, 5, 16), ((140, 20, 2), 0, 0, 0)]
 
 
