@@ -32,8 +32,7 @@ VARIANTS = ["fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "p
 # volume (the three-step kernel runs those on a copy of its march with the x
 # and y boundary rules folded), from fewer planes than the pipeline's depth
 # to several slabs
-INTERIOR_SHAPES = [(140, 27, 20), (200, 20, 3), (140, 20, 1), (260, 28, 40), (200, 36, 9),
-                       (140, 20, 100)]
+INTERIOR_SHAPES = [(140, 27, 20), (200, 20, 3), (132, 20, 100)]
 FOUR_PLANE = ("tb2", "tb2_h", "cube", "cube_32x8x2", "cube_64x8x1", "cube_8x8x8", "cube_32x4x4", "fused", "fused_nostream", "fused_h", "fused_nostream_h", "pair", "pair_nostream",
               "pair_h", "pair_nostream_h", "point", "gap", "gap_pair")
 

@@ -166,7 +166,7 @@ CASES = [((65, 9, 17), 0, 0, 0), ((64, 8, 48), 1, 0, 16), ((130, 17, 33), 0, 3, 
          ((66, 10, 18), 1, 2, 16), ((64, 8, 70), 0, 0, 32),
          # tiles whose whole halo lies inside the volume: several slabs, a
          # short grid, the 64-bit path, a shallow z
-         ((140, 27, 20), 0, 0, 8), ((200, 28, 40), 1, 5, 16), ((140, 20, 2), 0, 0, 0)]
+         ((140, 27, 20), 0, 0, 8), ((140, 27, 40), 1, 5, 16), ((140, 20, 2), 0, 0, 0)]
 
 
 @pytest.mark.parametrize("dims,wide,grid,planes", CASES, ids=lambda c: str(c))
@@ -206,7 +206,7 @@ CASES3 = [((65, 9, 17), 0, 0, 0), ((64, 8, 48), 1, 0, 16), ((130, 17, 33), 0, 3,
           ((1, 1, 40), 0, 0, 32), ((5, 70, 3), 0, 0, 0), ((63, 7, 15), 0, 0, 8), ((1, 1, 1), 0, 0, 0),
           ((66, 10, 18), 1, 2, 16), ((64, 8, 200), 0, 0, 96), ((70, 13, 9), 0, 0, 8),
           ((140, 27, 20), 0, 0, 8), ((200, 20, 12), 1, 3, 8), ((140, 20, 3), 0, 0, 0),
-          ((140, 20, 110), 0, 0, 96), ((200, 28, 40), 0, 5, 16)]
+          ((132, 20, 100), 0, 0, 96), ((140, 27, 40), 1, 5, 16)]
 
 
 def emulate3(func, tmp_path, kernel, b, p0, r0, lam, m, wide=0, grid=0, planes=0):
