@@ -8,13 +8,14 @@
 // by two voxels in x and y, step two on the tile grown by one, step three on
 // the tile, keeping the intermediate p and r on chip: b, p and r are read
 // once and p, r written once per three steps.  On MI355X at 512^3 a launch
-// takes 1.85 ms, 0.62 ms per step (two steps per pass: 0.75; one: 1.30); its
-// HBM traffic is 1.21 x the compulsory bytes, moved at 4.5 TB/s, and it
-// issues VALU instructions 65% of the time, so at two workgroups per CU the
-// pass is bound by instruction issue and latency together, not by memory
-// alone.  Most of the traffic above the compulsory bytes is the y-halo rows:
-// the tiles above and below run on the same XCD but drift apart by more
-// planes than its L2 holds.
+// takes 1.82-1.86 ms, 0.62 ms per step (two steps per pass: 0.75; one:
+// 1.30); its HBM traffic is 1.21 x the compulsory bytes, moved at 4.5 TB/s.
+// At two workgroups per CU it issues VALU instructions 63% of the time, and
+// the unit that hands load data back to the waves spends 68% of the launch
+// waiting for lines from the L1 and L2: the pass is bound by the latency of
+// its loads at this occupancy, not by bandwidth.  Most of the traffic above
+// the compulsory bytes is the y-halo rows: the tiles above and below run on
+// the same XCD but drift apart by more planes than its L2 holds.
 //
 // Every value is computed by the same device functions in the same order as
 // the one-step kernels (primal_z, dual_update), so three launches of those and
