@@ -401,17 +401,40 @@ __global__ __launch_bounds__(kTbBlock, 4) void tb3_kernel(
   }
 }
 
-// Planes per slab: the largest of 96, 64, 32 and 16 that still gives at
-// least 1024 tiles (two per workgroup slot at two workgroups per CU), else 8.
-// A slab re-reads 6 planes and runs 7 pipeline-filling iterations, so long
-// slabs pay off; at 512^3, 16 / 32 / 48 / 64 / 96 / 128 planes measured
-// 0.776 / 0.734 / 0.727 / 0.723 / 0.716 / 0.722 ms per step of a 20 x 10 run.
-inline int64_t tb3_planes(int64_t nx, int64_t ny, int64_t nz) {
+// Planes per slab, of 96, 64, 32, 16 and 8: the one with the least estimated
+// pass time (the longer on a tie).  A workgroup slot runs its tiles one after
+// another, a tile taking its planes + 7 plane steps (seven fill the pipeline).
+// When one slab layer's tiles fill the `slots` resident workgroups, the
+// layers run one after another and the pass takes about the sum over layers
+// of ceil(tiles per layer / slots) x (layer planes + 7); otherwise several
+// layers run side by side and it takes about ceil(tiles / slots) x (slab
+// planes + 7).  Long slabs re-read fewer planes and fill the pipeline less
+// often; short ones fill the chip when a layer has few tiles.  Measured per
+// three-step launch against the rule it replaced (the longest slab giving at
+// least 1024 tiles): 256^3 0.26 against 0.29 ms (64 against 32 planes),
+// 320^3 0.49 against 0.55 (64 against 32), 384^3 0.88 against 0.94 (32
+// against 96), 512 x 512 x 70 0.27 against 0.30 (one 70-plane slab against
+// 64 + 6); 448^3, 512^3 and 1000 x 777 x 301 keep 96 planes.
+inline int64_t tb3_planes(int64_t nx, int64_t ny, int64_t nz, int64_t slots = 512) {
   const int64_t txy = ((nx + kTbTileX - 1) / kTbTileX) * ((ny + kTbTileY - 1) / kTbTileY);
-  const int64_t choices[4] = {96, 64, 32, 16};
-  for (int i = 0; i < 4; ++i)
-    if (txy * ((nz + choices[i] - 1) / choices[i]) >= 1024) return choices[i];
-  return 8;
+  const int64_t choices[5] = {96, 64, 32, 16, 8};
+  int64_t best = 8, best_t = -1;
+  for (int i = 0; i < 5; ++i) {
+    const int64_t c = choices[i];
+    const int64_t layers = (nz + c - 1) / c;
+    int64_t t;
+    if (txy >= slots) {
+      const int64_t last = nz - (layers - 1) * c;
+      t = ((txy + slots - 1) / slots) * ((layers - 1) * (c + 7) + last + 7);
+    } else {
+      t = ((txy * layers + slots - 1) / slots) * ((c < nz ? c : nz) + 7);
+    }
+    if (best_t < 0 || t < best_t) {
+      best_t = t;
+      best = c;
+    }
+  }
+  return best;
 }
 
 }  // namespace tvfgp
