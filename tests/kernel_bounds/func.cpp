@@ -304,6 +304,13 @@ void run(const char *kernel, int64_t nx, int64_t ny, int64_t nz, float lam, floa
 }  // namespace
 
 int main(int argc, char **argv) {
+  // func slabs nx ny nz slots: the slab lengths the multi-step launchers pick
+  if (argc == 6 && !strcmp(argv[1], "slabs")) {
+    const int64_t nx = atoll(argv[2]), ny = atoll(argv[3]), nz = atoll(argv[4]);
+    printf("%lld %lld\n", (long long)tvfgp::tb3_planes(nx, ny, nz, atoll(argv[5])),
+           (long long)tvfgp::tb_planes(nx, ny, nz));
+    return 0;
+  }
   if (argc < 11 || argc > 13) {
     fprintf(stderr, "usage: func kernel nx ny nz lambda m1 m2 dir wide grid [planes [m3]]\n");
     return 2;

@@ -250,3 +250,37 @@ def test_three_steps_per_pass_binary16(func, tmp_path, dims, planes):
     assert np.array_equal(oracle.f32_to_f16_bits(pg), pe)
     assert np.array_equal(oracle.f32_to_f16_bits(rg), re)
 
+
+def slab_estimate(txy, nz, slots, c):
+    """The three-step launcher's estimate of a pass with c-plane slabs, in
+    plane steps: a tile of s planes takes s + 7; layers run one after another
+    when one fills the slots, else side by side."""
+    layers = (nz + c - 1) // c
+    if txy >= slots:
+        last = nz - (layers - 1) * c
+        return ((txy + slots - 1) // slots) * ((layers - 1) * (c + 7) + last + 7)
+    return ((txy * layers + slots - 1) // slots) * (min(c, nz) + 7)
+
+
+@pytest.mark.parametrize("dims,slots,want", [
+    ((512, 512, 512), 512, 96), ((1000, 777, 301), 512, 96), ((768, 768, 768), 512, 96),
+    ((448, 448, 448), 512, 96), ((512, 512, 70), 512, 96), ((384, 384, 384), 512, 32),
+    ((320, 320, 320), 512, 64), ((256, 256, 256), 512, 64), ((192, 192, 192), 512, 32),
+    ((128, 128, 128), 512, 8), ((32, 32, 32), 512, 8), ((256, 256, 256), 160, 32),
+    ((512, 512, 512), 160, 96), ((64, 8, 200), 512, 8)], ids=lambda c: str(c))
+def test_three_step_slab_length(func, dims, slots, want):
+    """tb3_planes takes, of 96, 64, 32, 16 and 8 planes, the slab with the least
+    estimated pass time (the longer on a tie); the expected values are the
+    measured best where the two rules differed (256^3, 320^3, 384^3, 192^3 and
+    the 512 x 512 x 70 shard)."""
+    nx, ny, nz = dims
+    r = subprocess.run([func, "slabs", str(nx), str(ny), str(nz), str(slots)],
+                       capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0, r.stderr
+    got = int(r.stdout.split()[0])
+    txy = ((nx + 63) // 64) * ((ny + 7) // 8)
+    best = min((96, 64, 32, 16, 8), key=lambda c: (slab_estimate(txy, nz, slots, c), -c))
+    assert got == best == want
+    # once one slab layer fills the chip, the longest slab is always taken
+    if txy >= slots:
+        assert got == 96
